@@ -1,0 +1,413 @@
+"""Float64 CPU oracle of the packed audio-video DiT block and the cached denoise loop.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg, never by the product path.
+
+Pages cited (by title and section):
+  [P1] TeleFuser PR #38, "perf(minimax-h3): add conservative DiT velocity reuse"
+  [P2] 1Cat-vLLM PR #584, "[Video] Add native H3 request-scoped TeaCache and Cache-DiT"
+  [P3] TeleFuser PR #23, "[FEAT] Add MiniMax H3 joint audio-video generation"
+
+The pages name the fused operations (RMSNorm with indexed AdaLN modulation, Q/K
+RMSNorm with NeoX RoPE, valid-only attention over a zero tail, SwiGLU) and the
+velocity-reuse cache policy, but print no formulas. Each function below is the
+plain textbook definition of the named operation; where a choice had to be made
+(chunk order, epsilon, which axis QK-norm runs over, the window convention of the
+cache) it is stated in the function's docstring.
+
+Pin status: every function is pinned by ``tests/test_oracle_pins.py`` against
+closed forms, brute-force scalar loops, special cases or the cache counts the
+pages print, except ``block_forward`` as a whole, whose composition is pinned
+only through its parts and a brute-force scalar re-derivation on a tiny shape
+("parity unpinned" against the pages: they print no numeric example of a block).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+# Order of the six AdaLN modulation rows of one modality.
+SHIFT_MSA, SCALE_MSA, GATE_MSA, SHIFT_MLP, SCALE_MLP, GATE_MLP = range(6)
+# Row classes of the packed sequence.
+VIDEO, AUDIO, TAIL = 0, 1, -1
+
+
+@dataclass(frozen=True)
+class Dims:
+    hidden: int
+    heads: int
+    head_dim: int
+    ffn: int
+    norm_eps: float = 1e-6
+    qk_eps: float = 1e-6
+    rope_base: float = 10000.0
+
+
+@dataclass(frozen=True)
+class Layout:
+    n_video: int
+    n_audio: int
+    seq_pad: int
+
+    @property
+    def n_valid(self) -> int:
+        return self.n_video + self.n_audio
+
+
+@dataclass(frozen=True)
+class CachePolicy:
+    mode: str = "off"  # "off" or "velocity" ("conservative" is an alias)
+    start_ratio: float = 0.2
+    end_ratio: float = 0.8
+    refresh_interval: int = 2
+    max_consecutive_reuse: int = 1
+    threshold: Optional[float] = None
+
+
+# ---------------------------------------------------------------- layout ----
+
+def row_modality(layout: Layout) -> np.ndarray:
+    """Modality id of every row of the packed sequence.
+
+    [P3 "Motivation", "Changes Made"]: one packed joint sequence of video and
+    audio tokens. [P1 §2]: the padded rows form a zero tail. Rows
+    0..n_video-1 are video (0), the next n_audio rows audio (1), the rest tail (-1).
+    """
+    m = np.full(layout.seq_pad, TAIL, dtype=np.int64)
+    m[: layout.n_video] = VIDEO
+    m[layout.n_video: layout.n_valid] = AUDIO
+    return m
+
+
+def row_positions(layout: Layout, positions: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rotary position of every row: the packed index unless an array is given."""
+    if positions is None:
+        return np.arange(layout.seq_pad, dtype=F64)
+    return np.asarray(positions, dtype=F64)
+
+
+# --------------------------------------------------------- elementwise ops --
+
+def bf16_round(a) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), returned as float64 values.
+
+    Used only where the contract itself converts to bf16: the DiT input made from
+    the fp32 latent at each refresh of the denoise loop ([P3 "Changes Made"]:
+    explicit BF16/FP32 boundaries).
+    """
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = rounded.astype(np.uint32).view(np.float32).astype(F64)
+    nan = np.isnan(f)
+    if nan.any():
+        out[nan] = np.nan
+    return out
+
+
+def rms_normalize(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis (RMSNorm without its gain)."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps)
+
+
+def silu(u: np.ndarray) -> np.ndarray:
+    """u * sigmoid(u) = u / (1 + exp(-u))."""
+    u = np.asarray(u, dtype=F64)
+    return u / (1.0 + np.exp(-u))
+
+
+# --------------------------------------------------------------- AdaLN ------
+
+def modulation_rows(ada: np.ndarray, temb: np.ndarray) -> np.ndarray:
+    """Per-modality modulation table E = A + T, shape [n_mod, 6, D].
+
+    [P1 §2] "RMSNorm fused with indexed AdaLN modulation"; [P3 "Changes Made"]
+    "indexed modulation" and independent per-modality schedules: each modality
+    carries its own timestep, so both the block's learned table A and the
+    timestep embedding T have one [6, D] slice per modality, and a row picks its
+    slice by modality id.
+    """
+    return np.asarray(ada, dtype=F64) + np.asarray(temb, dtype=F64)
+
+
+def norm_modulate(x, gain, E, modality, shift_chunk: int, scale_chunk: int, eps: float):
+    """h = RMSNorm(x) * g * (1 + scale[m]) + shift[m] per valid row; tail rows are 0.
+
+    [P1 §2] fused RMSNorm + indexed AdaLN; [P3 "Changes Made"] indexed modulation.
+    """
+    x = np.asarray(x, dtype=F64)
+    out = np.zeros_like(x)
+    valid = modality >= 0
+    if not valid.any():
+        return out
+    xn = rms_normalize(x[valid], eps) * np.asarray(gain, dtype=F64)
+    Em = E[modality[valid]]  # [V, 6, D]
+    out[valid] = xn * (1.0 + Em[:, scale_chunk]) + Em[:, shift_chunk]
+    return out
+
+
+# ------------------------------------------------------ attention pieces ----
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """x @ w^T with w in [out, in] layout, no bias."""
+    return np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+
+
+def qk_rms_norm(t: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head RMSNorm of q or k over head_dim: t [T, H, Dh], gain [Dh].
+
+    [P1 §2] and [P3 "Changes Made"]: Q/K RMSNorm before RoPE. Read as a per-head
+    norm (gain of length head_dim).
+    """
+    return rms_normalize(t, eps) * np.asarray(gain, dtype=F64)
+
+
+def rope_inv_freq(head_dim: int, base: float) -> np.ndarray:
+    """inv_i = base^(-2i / head_dim), i = 0 .. head_dim/2 - 1."""
+    i = np.arange(head_dim // 2, dtype=F64)
+    return np.power(F64(base), -2.0 * i / head_dim)
+
+
+def rope_neox(t: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """NeoX (rotate-half) rotary embedding of t [T, H, Dh] at positions pos [T].
+
+    [P3 "Changes Made"]: "NeoX RoPE". Element i of the first half and element
+    i + Dh/2 form one pair, rotated by the angle pos * inv_i:
+      out[i]        = t[i] cos - t[i+Dh/2] sin
+      out[i+Dh/2]   = t[i+Dh/2] cos + t[i] sin
+    """
+    t = np.asarray(t, dtype=F64)
+    half = t.shape[-1] // 2
+    theta = np.asarray(pos, dtype=F64)[:, None] * rope_inv_freq(t.shape[-1], base)[None, :]
+    c = np.cos(theta)[:, None, :]
+    s = np.sin(theta)[:, None, :]
+    a, b = t[..., :half], t[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def attention_valid(q, k, v, n_valid: int) -> np.ndarray:
+    """Softmax attention restricted to the valid prefix; q, k, v [L, H, Dh].
+
+    [P1 §2] valid-only attention with zero-tail merge: queries and keys with index
+    < n_valid attend to each other bidirectionally (jointly over both
+    modalities), with scores q.k / sqrt(Dh); output rows >= n_valid are 0. Rows of
+    the inputs at or beyond n_valid are never read.
+    """
+    q = np.asarray(q, dtype=F64)
+    L, H, Dh = q.shape
+    out = np.zeros((L, H, Dh), dtype=F64)
+    if n_valid == 0:
+        return out
+    qv = q[:n_valid].transpose(1, 0, 2)                           # [H, V, Dh]
+    kv = np.asarray(k, dtype=F64)[:n_valid].transpose(1, 0, 2)
+    vv = np.asarray(v, dtype=F64)[:n_valid].transpose(1, 0, 2)
+    s = (qv @ kv.transpose(0, 2, 1)) / math.sqrt(Dh)               # [H, V, V]
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    out[:n_valid] = (p @ vv).transpose(1, 0, 2)
+    return out
+
+
+def attention_rows(q_rows, k, v, n_valid: int) -> np.ndarray:
+    """Attention output for a subset of query rows q_rows [R, H, Dh] against the
+    valid keys k[:n_valid], v[:n_valid] (same definition as ``attention_valid``)."""
+    q_rows = np.asarray(q_rows, dtype=F64)
+    Dh = q_rows.shape[-1]
+    kv = np.asarray(k, dtype=F64)[:n_valid].transpose(1, 0, 2)     # [H, V, Dh]
+    vv = np.asarray(v, dtype=F64)[:n_valid].transpose(1, 0, 2)
+    qr = q_rows.transpose(1, 0, 2)                                 # [H, R, Dh]
+    s = (qr @ kv.transpose(0, 2, 1)) / math.sqrt(Dh)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return (p @ vv).transpose(1, 0, 2)
+
+
+def swiglu(h, w_gate_up, ffn: int) -> np.ndarray:
+    """SwiGLU: silu(h Wg^T) * (h Wu^T), with W_gate_up = [Wg; Wu] of shape [2F, D].
+
+    [P3 "Changes Made"]: fused SwiGLU. Gate rows come first in the packed weight.
+    """
+    w = np.asarray(w_gate_up, dtype=F64)
+    g = linear(h, w[:ffn])
+    u = linear(h, w[ffn:2 * ffn])
+    return silu(g) * u
+
+
+# ---------------------------------------------------------------- block -----
+
+def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
+                  positions: Optional[np.ndarray] = None,
+                  rows: Optional[np.ndarray] = None,
+                  want_intermediates: bool = False):
+    """One joint audio-video DiT block on the packed sequence x [L, D].
+
+    Composition (the pre-norm AdaLN DiT block that uses every fused operation the
+    pages list in [P1 §2] and [P3 "Changes Made"]):
+      E   = A + T                                   (per-modality table)
+      h   = RMSNorm(x) g1 (1 + E[m,1]) + E[m,0]
+      q,k,v = h Wqkv^T, split into heads
+      q,k = RoPE(QKNorm(q)), RoPE(QKNorm(k))
+      o   = valid-only attention(q, k, v)
+      x1  = x + E[m,2] * (o Wo^T)
+      h2  = RMSNorm(x1) g2 (1 + E[m,4]) + E[m,3]
+      x2  = x1 + E[m,5] * (SwiGLU(h2) Wd^T)
+    Tail rows of x2 are 0. With ``rows`` given, only those output rows are
+    computed (keys and values still come from every valid row).
+    """
+    D, H, Dh, F = dims.hidden, dims.heads, dims.head_dim, dims.ffn
+    x = np.asarray(x, dtype=F64)
+    L = layout.seq_pad
+    V = layout.n_valid
+    mod = row_modality(layout)
+    pos = row_positions(layout, positions)
+    E = modulation_rows(blk["ada"], temb)
+
+    h = norm_modulate(x, blk["norm1_g"], E, mod, SHIFT_MSA, SCALE_MSA, dims.norm_eps)
+    w_qkv = np.asarray(blk["w_qkv"], dtype=F64)
+    kv_rows = slice(0, V)
+    k = linear(h[kv_rows], w_qkv[D:2 * D]).reshape(V, H, Dh)
+    v = linear(h[kv_rows], w_qkv[2 * D:3 * D]).reshape(V, H, Dh)
+    k = rope_neox(qk_rms_norm(k, blk["k_g"], dims.qk_eps), pos[:V], dims.rope_base)
+
+    if rows is None:
+        rows = np.arange(L)
+    rows = np.asarray(rows, dtype=np.int64)
+    sel_valid = rows[rows < V]
+
+    q = linear(h[sel_valid], w_qkv[0:D]).reshape(len(sel_valid), H, Dh)
+    q = rope_neox(qk_rms_norm(q, blk["q_g"], dims.qk_eps), pos[sel_valid], dims.rope_base)
+    o = attention_rows(q, k, v, V).reshape(len(sel_valid), D) if V > 0 else np.zeros((0, D))
+
+    ms = mod[sel_valid]
+    Es = E[ms]                                              # [R, 6, D]
+    y = linear(o, blk["w_o"])
+    x1 = x[sel_valid] + Es[:, GATE_MSA] * y
+    x1n = rms_normalize(x1, dims.norm_eps) * np.asarray(blk["norm2_g"], dtype=F64)
+    h2 = x1n * (1.0 + Es[:, SCALE_MLP]) + Es[:, SHIFT_MLP]
+    a = swiglu(h2, blk["w_gate_up"], F)
+    z = linear(a, blk["w_down"])
+    x2_sel = x1 + Es[:, GATE_MLP] * z
+
+    out = np.zeros((len(rows), D), dtype=F64)
+    idx = np.nonzero(rows < V)[0]
+    out[idx] = x2_sel
+    if not want_intermediates:
+        return out
+    inter = dict(h=h[sel_valid], q=q.reshape(len(sel_valid), D), o=o, x1=x1, h2=h2, a=a,
+                 k=k.reshape(V, D), v=v.reshape(V, D), rows_valid=sel_valid)
+    return out, inter
+
+
+def stack_forward(x, blocks: Sequence[dict], temb, dims: Dims, layout: Layout,
+                  positions: Optional[np.ndarray] = None) -> np.ndarray:
+    """B blocks applied in order; the stack output is the velocity prediction."""
+    for blk in blocks:
+        x = block_forward(x, blk, temb, dims, layout, positions)
+    return x
+
+
+def useful_block_flops(n_valid: int, hidden: int, ffn: int) -> float:
+    """Useful matrix/attention FLOPs of one executed block over the valid tokens:
+    8VD^2 (QKV + out) + 6VDF (gate/up + down) + 4V^2D (scores + values).
+
+    [P2 "Purpose"]: only executed useful matrix/attention work counts toward
+    throughput; padded rows and skipped blocks add nothing.
+    """
+    V, D, F = float(n_valid), float(hidden), float(ffn)
+    return 8 * V * D * D + 6 * V * D * F + 4 * V * V * D
+
+
+# ------------------------------------------------------------ cache ---------
+
+def _policy_enabled(policy: CachePolicy) -> bool:
+    mode = policy.mode.lower()
+    if mode == "conservative":
+        mode = "velocity"
+    if mode not in ("off", "velocity"):
+        raise ValueError(f"unknown cache mode {policy.mode!r}")
+    if policy.threshold is not None:
+        raise NotImplementedError("threshold-based reuse is not defined on the pages")
+    return mode == "velocity"
+
+
+def cache_schedule(policy: CachePolicy, n_intervals: int) -> list:
+    """Hit (True) / refresh (False) flag of every denoise interval.
+
+    [P1 §3] MiniMaxH3DiTCacheConfig: reuse only inside [start_ratio, end_ratio)
+    of the denoising progress, a forced refresh every ``refresh_interval`` steps,
+    and at most ``max_consecutive_reuse`` reuses in a row. Progress of interval i
+    is i / N. A step reuses when a velocity exists, the step is in the window and
+    the current run of reuses is below min(max_consecutive_reuse,
+    refresh_interval - 1); otherwise it refreshes and the run restarts.
+    """
+    if not _policy_enabled(policy):
+        return [False] * n_intervals
+    cap = min(policy.max_consecutive_reuse, policy.refresh_interval - 1)
+    have_velocity = False
+    run = 0
+    flags = []
+    for i in range(n_intervals):
+        progress = i / n_intervals
+        in_window = policy.start_ratio <= progress < policy.end_ratio
+        if have_velocity and in_window and run < cap:
+            flags.append(True)
+            run += 1
+        else:
+            flags.append(False)
+            have_velocity = True
+            run = 0
+    return flags
+
+
+# ------------------------------------------------------------ Euler ---------
+
+def euler_step(x, v, modality, dt_video: float, dt_audio: float) -> np.ndarray:
+    """Flow-matching Euler update x + dt_m * v, with dt chosen by the row's modality.
+
+    [P3 "Motivation", "Changes Made"]: independent video and audio schedulers,
+    so each modality advances by its own sigma interval. Tail rows are left at 0.
+    """
+    x = np.asarray(x, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    out = np.zeros_like(x)
+    vid = modality == VIDEO
+    aud = modality == AUDIO
+    out[vid] = x[vid] + F64(dt_video) * v[vid]
+    out[aud] = x[aud] + F64(dt_audio) * v[aud]
+    return out
+
+
+def denoise_loop(x0, velocity: Callable[[int, np.ndarray], np.ndarray],
+                 sigmas_video, sigmas_audio, modality, hits: Sequence[bool]):
+    """Cached denoise loop over N = len(hits) intervals.
+
+    [P1 §3] on a hit the previous DiT-predicted velocity (both modalities) is
+    reused and the DiT call is skipped; on a refresh the DiT runs on the current
+    latent, converted to bf16 as the DiT input. Every interval then takes one
+    Euler step x_{i+1} = x_i + (sigma_m[i+1] - sigma_m[i]) v. Returns the final
+    latent and the list of velocities the DiT produced (one per refresh).
+    """
+    x = np.asarray(x0, dtype=F64).copy()
+    v = None
+    produced = []
+    for i, hit in enumerate(hits):
+        if hit:
+            if v is None:
+                raise ValueError("a hit before any refresh")
+        else:
+            v = np.asarray(velocity(i, bf16_round(x)), dtype=F64)
+            produced.append(v)
+        dt_v = F64(sigmas_video[i + 1]) - F64(sigmas_video[i])
+        dt_a = F64(sigmas_audio[i + 1]) - F64(sigmas_audio[i])
+        x = euler_step(x, v, modality, dt_v, dt_a)
+    return x, produced

@@ -1,0 +1,503 @@
+"""Pins of the float64 oracle against things other than itself.
+
+Each test checks an oracle function against a value the pages print, a closed
+form, a symmetry, a special case that reduces to a textbook routine, or a
+brute-force scalar-loop computation written independently here. They run on
+the CPU only.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ cache ---------
+
+def _policy(mode="conservative", s=0.2, e=0.8, r=2, c=1, threshold=None):
+    return O.CachePolicy(mode=mode, start_ratio=s, end_ratio=e, refresh_interval=r,
+                         max_consecutive_reuse=c, threshold=threshold)
+
+
+def test_cache_counts_printed_on_pages():
+    """49 intervals: cache off gives 49 calls / 0 hits, conservative 34 / 15."""
+    with open(os.path.join(GOLDEN, "cache_counts.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        pol = _policy(case["mode"], case["start_ratio"], case["end_ratio"],
+                      case["refresh_interval"], case["max_consecutive_reuse"])
+        flags = O.cache_schedule(pol, g["n_intervals"])
+        assert sum(flags) == case["cache_hits"]
+        assert len(flags) - sum(flags) == case["dit_calls"]
+
+
+def test_cache_velocity_alias_and_unknown_mode():
+    a = O.cache_schedule(_policy("velocity"), 49)
+    b = O.cache_schedule(_policy("conservative"), 49)
+    assert a == b
+    with pytest.raises(ValueError):
+        O.cache_schedule(_policy("bogus"), 49)
+    with pytest.raises(NotImplementedError):
+        O.cache_schedule(_policy(threshold=0.1), 49)
+
+
+@pytest.mark.parametrize("n", list(range(1, 121)))
+def test_cache_invariants(n):
+    flags = O.cache_schedule(_policy(), n)
+    assert len(flags) == n
+    if n:
+        assert not flags[0], "the first interval has no velocity to reuse"
+    for i in range(1, n):
+        assert not (flags[i] and flags[i - 1]), "at most one reuse in a row"
+    for i, f in enumerate(flags):
+        if f:
+            assert 0.2 <= i / n < 0.8, "reuse only inside the window"
+    # every in-window step whose predecessor refreshed is a hit (greedy reuse)
+    for i in range(1, n):
+        if 0.2 <= i / n < 0.8 and not flags[i - 1]:
+            assert flags[i]
+
+
+def test_cache_degenerate_policies():
+    for n in (1, 2, 7, 49, 50):
+        assert sum(O.cache_schedule(_policy(r=1), n)) == 0
+        assert sum(O.cache_schedule(_policy(c=0), n)) == 0
+        assert sum(O.cache_schedule(_policy(s=0.5, e=0.5), n)) == 0
+        assert sum(O.cache_schedule(_policy(mode="off"), n)) == 0
+        # full window, refresh every 2nd step: every odd step reuses
+        full = O.cache_schedule(_policy(s=0.0, e=1.0), n)
+        assert sum(full) == n // 2
+        assert full == [i % 2 == 1 for i in range(n)]
+        # refresh every 3rd step with up to 2 reuses: pattern R H H R H H ...
+        three = O.cache_schedule(_policy(s=0.0, e=1.0, r=3, c=5), n)
+        assert three == [i % 3 != 0 for i in range(n)]
+
+
+def test_cache_hit_set_at_49():
+    flags = O.cache_schedule(_policy(), 49)
+    assert [i for i, f in enumerate(flags) if f] == list(range(10, 39, 2))
+
+
+# ------------------------------------------------------------ bf16 ----------
+
+def test_bf16_round_ties_to_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 1.0 + 2 ** -7,
+                     1.0 + 2 ** -8 + 2 ** -20, 1.0 / 3.0, 0.0, -0.0], dtype=np.float64)
+    want = [1.0, 1.0, 1.0 + 2 ** -6, -1.0, 1.0 + 2 ** -7, 1.0 + 2 ** -7, 0.333984375, 0.0, -0.0]
+    got = O.bf16_round(vals)
+    assert list(got) == want
+    assert math.copysign(1.0, got[-1]) == -1.0
+
+
+# ---------------------------------------------------- RMSNorm + AdaLN -------
+
+def test_rms_normalize_constant_row():
+    for c in (0.5, 2.0, -3.0, 1e-4):
+        x = np.full((1, 16), c)
+        got = O.rms_normalize(x, 1e-6)
+        assert np.allclose(got, c / math.sqrt(c * c + 1e-6), rtol=1e-15, atol=0)
+
+
+def test_norm_modulate_identity_modulation_rms():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((9, 32))
+    mod = np.array([0, 0, 0, 0, 1, 1, 1, -1, -1])
+    E = np.zeros((2, 6, 32))
+    h = O.norm_modulate(x, np.ones(32), E, mod, 0, 1, 1e-6)
+    ms = np.mean(x[:7] ** 2, axis=1)
+    rms = np.sqrt(np.mean(h[:7] ** 2, axis=1))
+    assert np.allclose(rms, np.sqrt(ms / (ms + 1e-6)), rtol=1e-14)
+    assert np.all(h[7:] == 0)
+
+
+def test_norm_modulate_closed_form_and_modality_tables():
+    # one row, constant c, scale s, shift b, gain g: g*c/sqrt(c^2+eps)*(1+s)+b
+    D = 8
+    E = np.zeros((2, 6, D))
+    E[0, 1] = 0.5
+    E[0, 0] = -0.25
+    E[1, 1] = -0.5
+    E[1, 0] = 2.0
+    g = np.full(D, 3.0)
+    x = np.full((3, D), 2.0)
+    mod = np.array([0, 1, -1])
+    h = O.norm_modulate(x, g, E, mod, 0, 1, 1e-6)
+    n = 3.0 * 2.0 / math.sqrt(4.0 + 1e-6)
+    assert np.allclose(h[0], n * 1.5 - 0.25, rtol=1e-15)
+    assert np.allclose(h[1], n * 0.5 + 2.0, rtol=1e-15)
+    assert np.all(h[2] == 0)
+
+
+def test_norm_modulate_modality_swap_symmetry():
+    rng = np.random.default_rng(2)
+    D = 16
+    x = rng.standard_normal((6, D))
+    E = rng.standard_normal((2, 6, D))
+    mod = np.array([0, 0, 0, 1, 1, 1])
+    h = O.norm_modulate(x, np.ones(D), E, mod, 0, 1, 1e-6)
+    h_sw = O.norm_modulate(x, np.ones(D), E[::-1], 1 - mod, 0, 1, 1e-6)
+    assert np.array_equal(h, h_sw)
+    same = O.norm_modulate(x, np.ones(D), np.stack([E[0], E[0]]), mod, 0, 1, 1e-6)
+    ref = O.norm_modulate(x, np.ones(D), np.stack([E[0], E[0]]), np.zeros(6, int), 0, 1, 1e-6)
+    assert np.array_equal(same, ref)
+
+
+def test_modulation_rows_is_sum():
+    a = np.arange(24.0).reshape(2, 6, 2)
+    t = np.ones((2, 6, 2)) * 0.5
+    assert np.array_equal(O.modulation_rows(a, t), a + 0.5)
+
+
+# ------------------------------------------------------------ RoPE ----------
+
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(3)
+    t = rng.standard_normal((1, 3, 64))
+    assert np.allclose(O.rope_neox(t, np.zeros(1), 1e4), t, rtol=0, atol=0)
+
+
+def test_rope_rotation_matrix_and_pairing():
+    # head_dim 2: a plain 2-D rotation by angle pos (inv_0 = 1)
+    for p in (0.3, 1.0, 2.5, 100.0):
+        q = np.array([[[0.7, -1.3]]])
+        c, s = math.cos(p), math.sin(p)
+        want = np.array([0.7 * c + 1.3 * s, -1.3 * c + 0.7 * s])
+        assert np.allclose(O.rope_neox(q, np.array([p]), 1e4)[0, 0], want, rtol=1e-15)
+    # head_dim 4, base 100: inv = [1, 0.1]; NeoX pairs (0,2) and (1,3)
+    e1 = np.zeros((1, 1, 4))
+    e1[0, 0, 1] = 1.0
+    out = O.rope_neox(e1, np.array([3.0]), 100.0)[0, 0]
+    assert np.allclose(out, [0.0, math.cos(0.3), 0.0, math.sin(0.3)], atol=1e-15)
+    e0 = np.zeros((1, 1, 4))
+    e0[0, 0, 2] = 1.0
+    out = O.rope_neox(e0, np.array([3.0]), 100.0)[0, 0]
+    assert np.allclose(out, [-math.sin(3.0), 0.0, math.cos(3.0), 0.0], atol=1e-15)
+
+
+def test_rope_preserves_pair_norms_and_is_relative():
+    rng = np.random.default_rng(4)
+    Dh = 128
+    q = rng.standard_normal((5, 2, Dh))
+    k = rng.standard_normal((5, 2, Dh))
+    pos = np.array([0.0, 1.0, 17.0, 4000.0, 32767.0])
+    rq = O.rope_neox(q, pos, 1e4)
+    half = Dh // 2
+    n0 = q[..., :half] ** 2 + q[..., half:] ** 2
+    n1 = rq[..., :half] ** 2 + rq[..., half:] ** 2
+    assert np.allclose(n0, n1, rtol=1e-12)
+    # <R(q, m), R(k, n)> depends only on m - n
+    m = np.array([3.0, 10.0, 250.0])
+    nn = np.array([1.0, 30.0, 7.0])
+    a = np.sum(O.rope_neox(q[:3], m, 1e4) * O.rope_neox(k[:3], nn, 1e4), axis=-1)
+    b = np.sum(O.rope_neox(q[:3], m + 1000, 1e4) * O.rope_neox(k[:3], nn + 1000, 1e4), axis=-1)
+    assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+def test_qk_rms_norm_per_head():
+    t = np.zeros((1, 2, 4))
+    t[0, 0] = [1, 1, 1, 1]
+    t[0, 1] = [2, 0, 0, 0]
+    g = np.array([1.0, 2.0, 3.0, 4.0])
+    out = O.qk_rms_norm(t, g, 0.0)
+    assert np.allclose(out[0, 0], g)
+    assert np.allclose(out[0, 1], [2.0, 0, 0, 0])  # 2 / sqrt(4/4) * 1
+
+
+# ------------------------------------------------------------ attention -----
+
+def _attn_brute(q, k, v, n_valid):
+    L, H, Dh = q.shape
+    out = [[[0.0] * Dh for _ in range(H)] for _ in range(L)]
+    for h in range(H):
+        for i in range(n_valid):
+            scores = []
+            for j in range(n_valid):
+                s = 0.0
+                for d in range(Dh):
+                    s += float(q[i, h, d]) * float(k[j, h, d])
+                scores.append(s / math.sqrt(Dh))
+            mx = max(scores)
+            w = [math.exp(s - mx) for s in scores]
+            tot = sum(w)
+            for d in range(Dh):
+                out[i][h][d] = sum(w[j] * float(v[j, h, d]) for j in range(n_valid)) / tot
+    return np.array(out)
+
+
+@pytest.mark.parametrize("L,n_valid,H,Dh", [(7, 5, 2, 4), (9, 9, 1, 8), (12, 1, 3, 2), (6, 0, 1, 4)])
+def test_attention_against_brute_force(L, n_valid, H, Dh):
+    rng = np.random.default_rng(5 + L)
+    q, k, v = (rng.standard_normal((L, H, Dh)) for _ in range(3))
+    got = O.attention_valid(q, k, v, n_valid)
+    want = _attn_brute(q, k, v, n_valid)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert np.all(got[n_valid:] == 0)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(6)
+    q, k, v = (rng.standard_normal((8, 2, 4)) for _ in range(3))
+    # one valid key: output is that key's value
+    assert np.allclose(O.attention_valid(q, k, v, 1)[0], v[0], rtol=1e-15)
+    # identical keys: output is the mean of the values
+    k_same = np.repeat(k[:1], 8, axis=0)
+    assert np.allclose(O.attention_valid(q, k_same, v, 6)[:6],
+                       np.broadcast_to(v[:6].mean(axis=0), (6, 2, 4)), rtol=1e-13)
+    # garbage in the masked tail changes nothing
+    kg, vg, qg = k.copy(), v.copy(), q.copy()
+    kg[5:] = 1e30
+    vg[5:] = np.nan
+    qg[5:] = -7.0
+    assert np.array_equal(O.attention_valid(q, k, v, 5), O.attention_valid(qg, kg, vg, 5))
+    # rows-subset form agrees with the full form
+    full = O.attention_valid(q, k, v, 7)
+    sub = O.attention_rows(q[[0, 3, 6]], k, v, 7)
+    assert np.allclose(sub, full[[0, 3, 6]], rtol=1e-14)
+
+
+def test_attention_two_key_closed_form():
+    # q.k0 = 4, q.k1 = 0 at Dh = 4: scores 2 and 0 after the 1/sqrt(Dh) scale
+    q = np.zeros((2, 1, 4))
+    q[0, 0, 0] = 2.0
+    k = np.zeros((2, 1, 4))
+    k[0, 0, 0] = 2.0
+    v = np.zeros((2, 1, 4))
+    v[0, 0, 1] = 1.0
+    v[1, 0, 2] = 1.0
+    o = O.attention_valid(q, k, v, 2)[0, 0]
+    w0 = math.exp(2.0) / (math.exp(2.0) + 1.0)
+    assert np.allclose(o, [0.0, w0, 1.0 - w0, 0.0], rtol=1e-15)
+
+
+# ------------------------------------------------------------ SwiGLU --------
+
+def test_silu_values():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert math.isclose(O.silu(np.array([1.0]))[0], 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    assert math.isclose(O.silu(np.array([-1.0]))[0], -1.0 / (1.0 + math.exp(1.0)), rel_tol=1e-15)
+
+
+def test_swiglu_gate_rows_first():
+    h = np.array([[2.0]])
+    w = np.array([[1.0], [3.0]])  # gate row 1, up row 3
+    got = O.swiglu(h, w, 1)[0, 0]
+    assert math.isclose(got, (2.0 / (1.0 + math.exp(-2.0))) * 6.0, rel_tol=1e-15)
+
+
+# -------------------------------------------------------- block (brute) -----
+
+def _block_brute(x, blk, temb, D, H, Dh, F, n_video, n_audio, L, eps, qk_eps, base, count):
+    """Scalar-loop block written directly from the block's definition."""
+    V = n_video + n_audio
+
+    def mod_of(r):
+        return 0 if r < n_video else 1
+
+    def E(m, c, d):
+        return float(blk["ada"][m, c, d]) + float(temb[m, c, d])
+
+    def rmsn(row, g):
+        ms = sum(t * t for t in row) / len(row)
+        inv = 1.0 / math.sqrt(ms + eps)
+        return [row[i] * inv * g[i] for i in range(len(row))]
+
+    def matvec(w, vec, rows_out):
+        out = []
+        for o in range(rows_out):
+            acc = 0.0
+            for i in range(len(vec)):
+                acc += float(w[o, i]) * vec[i]
+                count[0] += 2
+            out.append(acc)
+        return out
+
+    hs, qs, ks, vs = [], [], [], []
+    for r in range(V):
+        m = mod_of(r)
+        n = rmsn([float(t) for t in x[r]], blk["norm1_g"])
+        h = [n[d] * (1.0 + E(m, 1, d)) + E(m, 0, d) for d in range(D)]
+        qkv = matvec(blk["w_qkv"], h, 3 * D)
+        per = []
+        for part in range(2):
+            vec = qkv[part * D:(part + 1) * D]
+            g = blk["q_g"] if part == 0 else blk["k_g"]
+            heads = []
+            for hh in range(H):
+                hv = vec[hh * Dh:(hh + 1) * Dh]
+                ms = sum(t * t for t in hv) / Dh
+                hv = [hv[i] / math.sqrt(ms + qk_eps) * g[i] for i in range(Dh)]
+                rot = [0.0] * Dh
+                for i in range(Dh // 2):
+                    ang = r * base ** (-2.0 * i / Dh)
+                    c, s = math.cos(ang), math.sin(ang)
+                    rot[i] = hv[i] * c - hv[i + Dh // 2] * s
+                    rot[i + Dh // 2] = hv[i + Dh // 2] * c + hv[i] * s
+                heads.append(rot)
+            per.append(heads)
+        qs.append(per[0])
+        ks.append(per[1])
+        vs.append([qkv[2 * D + hh * Dh: 2 * D + (hh + 1) * Dh] for hh in range(H)])
+        hs.append(h)
+    out = np.zeros((L, D))
+    for r in range(V):
+        m = mod_of(r)
+        o = []
+        for hh in range(H):
+            sc = []
+            for j in range(V):
+                sc.append(sum(qs[r][hh][d] * ks[j][hh][d] for d in range(Dh)) / math.sqrt(Dh))
+                count[0] += 2 * Dh
+            mx = max(sc)
+            w = [math.exp(t - mx) for t in sc]
+            tot = sum(w)
+            for d in range(Dh):
+                o.append(sum(w[j] * vs[j][hh][d] for j in range(V)) / tot)
+                count[0] += 2 * V
+        y = matvec(blk["w_o"], o, D)
+        x1 = [float(x[r, d]) + E(m, 2, d) * y[d] for d in range(D)]
+        n2 = rmsn(x1, blk["norm2_g"])
+        h2 = [n2[d] * (1.0 + E(m, 4, d)) + E(m, 3, d) for d in range(D)]
+        gu = matvec(blk["w_gate_up"], h2, 2 * F)
+        a = [gu[i] / (1.0 + math.exp(-gu[i])) * gu[F + i] for i in range(F)]
+        z = matvec(blk["w_down"], a, D)
+        for d in range(D):
+            out[r, d] = x1[d] + E(m, 5, d) * z[d]
+    return out
+
+
+def _tiny_block(seed, D=8, H=2, Dh=4, F=6, gains_random=True):
+    rng = np.random.default_rng(seed)
+    blk = dict(w_qkv=rng.standard_normal((3 * D, D)) * 0.3,
+               w_o=rng.standard_normal((D, D)) * 0.3,
+               w_gate_up=rng.standard_normal((2 * F, D)) * 0.3,
+               w_down=rng.standard_normal((D, F)) * 0.3,
+               norm1_g=1 + 0.1 * rng.standard_normal(D) if gains_random else np.ones(D),
+               norm2_g=1 + 0.1 * rng.standard_normal(D) if gains_random else np.ones(D),
+               q_g=1 + 0.1 * rng.standard_normal(Dh) if gains_random else np.ones(Dh),
+               k_g=1 + 0.1 * rng.standard_normal(Dh) if gains_random else np.ones(Dh),
+               ada=0.2 * rng.standard_normal((2, 6, D)))
+    temb = rng.standard_normal((2, 6, D))
+    return blk, temb
+
+
+def test_block_against_scalar_loops():
+    D, H, Dh, F = 8, 2, 4, 6
+    n_v, n_a, L = 3, 2, 7
+    blk, temb = _tiny_block(7, D, H, Dh, F)
+    rng = np.random.default_rng(8)
+    x = np.zeros((L, D))
+    x[: n_v + n_a] = rng.standard_normal((n_v + n_a, D))
+    dims = O.Dims(D, H, Dh, F, rope_base=100.0)
+    lay = O.Layout(n_v, n_a, L)
+    got = O.block_forward(x, blk, temb, dims, lay)
+    count = [0]
+    want = _block_brute(x, blk, temb, D, H, Dh, F, n_v, n_a, L, 1e-6, 1e-6, 100.0, count)
+    assert np.allclose(got, want, rtol=1e-11, atol=1e-12)
+    assert np.all(got[n_v + n_a:] == 0)
+    # the FLOP formula equals the multiply-adds the scalar loops executed
+    assert O.useful_block_flops(n_v + n_a, D, F) == count[0]
+    # subset rows agree with the full result
+    sub = O.block_forward(x, blk, temb, dims, lay, rows=np.array([0, 4, 6]))
+    assert np.allclose(sub, got[[0, 4, 6]], rtol=1e-13, atol=1e-14)
+
+
+def test_block_zero_gates_is_identity():
+    D, H, Dh, F = 8, 2, 4, 6
+    blk, temb = _tiny_block(9, D, H, Dh, F)
+    blk["ada"][:, 2] = 0.0
+    blk["ada"][:, 5] = 0.0
+    temb[:, 2] = 0.0
+    temb[:, 5] = 0.0
+    rng = np.random.default_rng(10)
+    x = np.zeros((6, D))
+    x[:5] = rng.standard_normal((5, D))
+    out = O.block_forward(x, blk, temb, O.Dims(D, H, Dh, F), O.Layout(2, 3, 6))
+    assert np.array_equal(out[:5], x[:5])
+    assert np.all(out[5:] == 0)
+
+
+def test_block_tail_values_do_not_leak():
+    D, H, Dh, F = 8, 2, 4, 6
+    blk, temb = _tiny_block(11, D, H, Dh, F)
+    rng = np.random.default_rng(12)
+    x = np.zeros((9, D))
+    x[:6] = rng.standard_normal((6, D))
+    a = O.block_forward(x, blk, temb, O.Dims(D, H, Dh, F), O.Layout(4, 2, 9))
+    x[6:] = 1e6
+    b = O.block_forward(x, blk, temb, O.Dims(D, H, Dh, F), O.Layout(4, 2, 9))
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------ loop ----------
+
+def test_euler_constant_velocity_closed_form():
+    sv = np.array([1.0, 0.75, 0.5, 0.25, 0.0], dtype=np.float32)
+    sa = np.array([1.0, 0.5, 0.4, 0.1, 0.0], dtype=np.float32)
+    mod = np.array([0, 0, 1, -1])
+    x0 = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [0.0, 0.0]])
+    v = np.array([[0.5, -1.0], [2.0, 0.0], [1.0, 1.0], [9.0, 9.0]])
+    for hits in ([False] * 4, [False, True, False, True]):
+        xN, prod = O.denoise_loop(x0, lambda i, xb: v, sv, sa, mod, hits)
+        assert np.allclose(xN[:2], x0[:2] - v[:2], rtol=1e-15)   # sigma_N - sigma_0 = -1
+        assert np.allclose(xN[2], x0[2] - v[2], rtol=1e-15)
+        assert np.all(xN[3] == 0)
+        assert len(prod) == 4 - sum(hits)
+
+
+def test_loop_reuses_the_last_refresh_and_rounds_input():
+    n = 49
+    sv = np.linspace(1, 0, n + 1).astype(np.float32)
+    sv[-1] = 0
+    sa = sv
+    flags = O.cache_schedule(O.CachePolicy(mode="conservative"), n)
+    mod = np.array([0, 1])
+    x0 = np.array([[1.0 / 3.0], [-0.7]])
+    seen = []
+
+    def vel(i, xb):
+        seen.append((i, xb.copy()))
+        return np.full_like(xb, float(i + 1))
+
+    xN, _ = O.denoise_loop(x0, vel, sv, sa, mod, flags)
+    # closed form: x_N = x_0 + sum_i dt_i (r(i) + 1), r(i) the last refresh <= i
+    r, acc = -1, 0.0
+    for i in range(n):
+        if not flags[i]:
+            r = i
+        acc += (float(sv[i + 1]) - float(sv[i])) * (r + 1)
+    assert np.allclose(xN[:, 0], x0[:, 0] + acc, rtol=1e-14)
+    assert [i for i, _ in seen] == [i for i in range(n) if not flags[i]]
+    # the first DiT input is bf16(x_0): 1/3 -> 0x3EAB = 0.333984375
+    assert seen[0][1][0, 0] == 0.333984375
+
+
+def test_loop_linear_stub_closed_form():
+    # v = a * x with x a power-of-two multiple kept exact: x0 = 1, a = -1, dt = -1/4
+    sv = np.array([1.0, 0.75, 0.5, 0.25, 0.0], dtype=np.float32)
+    mod = np.array([0])
+    flags = [False, True, False, True]
+    x0 = np.array([[1.0]])
+    xN, _ = O.denoise_loop(x0, lambda i, xb: -1.0 * xb, sv, sv, mod, flags)
+    # c_{i+1} = c_i + dt * a * c_{r(i)}, computed here with exact fractions
+    from fractions import Fraction
+    c = [Fraction(1)]
+    r = 0
+    for i in range(4):
+        if not flags[i]:
+            r = i
+        c.append(c[-1] + Fraction(-1, 4) * Fraction(-1) * c[r])
+    # every c_r is a dyadic rational with few bits, so bf16 rounding is exact here
+    assert xN[0, 0] == float(c[-1])
+
+
+def test_euler_per_modality_dt():
+    x = np.array([[1.0], [1.0], [1.0]])
+    v = np.array([[2.0], [2.0], [2.0]])
+    out = O.euler_step(x, v, np.array([0, 1, -1]), -0.25, -0.5)
+    assert np.array_equal(out[:, 0], [0.5, 0.0, 0.0])
