@@ -1,0 +1,440 @@
+// C-ABI of the joint audio-video DiT denoising step: argument validation, the host-side cache
+// schedule, the block composer and the denoise loop. Everything here is host code; every step
+// of the math runs in the HIP kernels declared in kernels.hpp.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/avdit.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int32_t kMaxSeq = 1 << 20;
+constexpr int32_t kMaxHidden = 8192;
+constexpr int32_t kMaxFfn = 65536;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_dims(const dit_dims* d) {
+  if (!d) return fail(DIT_ERR_INVALID, "dims is null");
+  if (d->hidden <= 0 || d->heads <= 0 || d->head_dim <= 0 || d->ffn <= 0)
+    return fail(DIT_ERR_INVALID, "dims must be positive (hidden %d, heads %d, head_dim %d, ffn %d)",
+                d->hidden, d->heads, d->head_dim, d->ffn);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if ((int64_t)d->heads * d->head_dim != d->hidden)
+    return fail(DIT_ERR_INVALID, "hidden %d != heads %d * head_dim %d", d->hidden, d->heads,
+                d->head_dim);
+  if (d->hidden > kMaxHidden)
+    return fail(DIT_ERR_UNSUPPORTED, "hidden %d exceeds %d", d->hidden, kMaxHidden);
+  if (d->ffn > kMaxFfn) return fail(DIT_ERR_UNSUPPORTED, "ffn %d exceeds %d", d->ffn, kMaxFfn);
+  if (d->n_mod != 2)
+    return fail(DIT_ERR_UNSUPPORTED, "n_mod %d is not supported (video + audio = 2)", d->n_mod);
+  if (!(d->norm_eps >= 0.0f) || !std::isfinite(d->norm_eps) || !(d->qk_eps >= 0.0f) ||
+      !std::isfinite(d->qk_eps))
+    return fail(DIT_ERR_INVALID, "epsilons must be finite and >= 0");
+  if (!(d->rope_base > 0.0f) || !std::isfinite(d->rope_base))
+    return fail(DIT_ERR_INVALID, "rope_base must be finite and > 0");
+  return DIT_OK;
+}
+
+int check_layout(const dit_layout* l) {
+  if (!l) return fail(DIT_ERR_INVALID, "layout is null");
+  if (l->n_video < 0 || l->n_audio < 0 || l->seq_pad < 0)
+    return fail(DIT_ERR_INVALID, "layout counts must be >= 0");
+  if ((int64_t)l->n_video + l->n_audio > l->seq_pad)
+    return fail(DIT_ERR_INVALID, "seq_pad %d < n_video %d + n_audio %d", l->seq_pad, l->n_video,
+                l->n_audio);
+  if (l->seq_pad > kMaxSeq) return fail(DIT_ERR_UNSUPPORTED, "seq_pad %d exceeds %d", l->seq_pad, kMaxSeq);
+  return DIT_OK;
+}
+
+int check_policy(const dit_cache_policy* p) {
+  if (!p) return fail(DIT_ERR_INVALID, "policy is null");
+  if (p->mode != DIT_CACHE_OFF && p->mode != DIT_CACHE_VELOCITY)
+    return fail(DIT_ERR_UNSUPPORTED, "cache mode %d is not supported", p->mode);
+  if (!(p->start_ratio >= 0.0 && p->start_ratio <= 1.0) ||
+      !(p->end_ratio >= 0.0 && p->end_ratio <= 1.0))
+    return fail(DIT_ERR_INVALID, "cache ratios must lie in [0, 1]");
+  if (p->start_ratio > p->end_ratio) return fail(DIT_ERR_INVALID, "start_ratio > end_ratio");
+  if (p->refresh_interval < 1) return fail(DIT_ERR_INVALID, "refresh_interval must be >= 1");
+  if (p->max_consecutive_reuse < 0)
+    return fail(DIT_ERR_INVALID, "max_consecutive_reuse must be >= 0");
+  if (!std::isnan(p->threshold))
+    return fail(DIT_ERR_UNSUPPORTED, "a reuse threshold is not supported (only None)");
+  return DIT_OK;
+}
+
+// Greedy reuse rule of MiniMaxH3DiTCacheConfig (TeleFuser PR #38, section 3): interval i at
+// progress i/N reuses when a velocity exists, i/N lies in [start, end) and fewer than
+// min(max_consecutive_reuse, refresh_interval - 1) reuses happened since the last refresh.
+void schedule(const dit_cache_policy* p, int32_t n, uint8_t* hit) {
+  if (p->mode == DIT_CACHE_OFF) {
+    if (n > 0) std::memset(hit, 0, (size_t)n);
+    return;
+  }
+  const int32_t cap = p->max_consecutive_reuse < p->refresh_interval - 1 ? p->max_consecutive_reuse
+                                                                         : p->refresh_interval - 1;
+  bool have = false;
+  int32_t run = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const double progress = (double)i / (double)n;
+    const bool in_window = progress >= p->start_ratio && progress < p->end_ratio;
+    if (have && in_window && run < cap) {
+      hit[i] = 1;
+      ++run;
+    } else {
+      hit[i] = 0;
+      have = true;
+      run = 0;
+    }
+  }
+}
+
+int64_t ffn_ld(const dit_dims* d) { return ((int64_t)d->ffn + 7) / 8 * 8; }
+
+void build_map(const dit_dims* d, const dit_layout* l, int32_t n_blocks, dit_workspace_map* m) {
+  const size_t L = (size_t)l->seq_pad, D = (size_t)d->hidden;
+  const size_t row_d = align_up(L * D * 2);
+  size_t off = 0;
+  m->h = off; off += row_d;
+  m->qkv = off; off += align_up(L * 3 * D * 2);
+  m->attn_out = off; off += row_d;
+  m->x1 = off; off += align_up(L * D * 4);
+  m->h2 = off; off += row_d;
+  m->ffn_ld = ffn_ld(d);
+  m->act = off; off += align_up(L * (size_t)m->ffn_ld * 2);
+  if (n_blocks >= 1) {
+    m->x_bf16 = off; off += row_d;
+    m->ping = off; off += row_d;
+    m->pong = off; off += row_d;
+    m->velocity = off; off += row_d;
+  } else {
+    m->x_bf16 = m->ping = m->pong = m->velocity = 0;
+  }
+  m->total = off < kAlign ? kAlign : off;
+}
+
+int check_weights(const dit_block_weights* w, int idx) {
+  if (!w) return fail(DIT_ERR_INVALID, "block %d weights are null", idx);
+  if (!w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->norm1_g || !w->norm2_g ||
+      !w->q_g || !w->k_g || !w->ada)
+    return fail(DIT_ERR_INVALID, "block %d has a null weight pointer", idx);
+  return DIT_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DIT_OK;
+  return fail(DIT_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Enqueue one block on `s`: eight launches, no host synchronisation.
+int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weights* w,
+                  const float* temb, const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode,
+                  char* ws, const dit_workspace_map& m, hipStream_t s) {
+  using namespace avdit;
+  const int32_t D = d->hidden, F = d->ffn, L = l->seq_pad;
+  const RowLayout rows{l->n_video, l->n_video + l->n_audio, L};
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + m.h);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(ws + m.qkv);
+  uint16_t* att = reinterpret_cast<uint16_t*>(ws + m.attn_out);
+  float* x1 = reinterpret_cast<float*>(ws + m.x1);
+  uint16_t* h2 = reinterpret_cast<uint16_t*>(ws + m.h2);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + m.act);
+  int st;
+
+  NormModArgs n1{};
+  n1.x = x_in; n1.h = h; n1.gain = w->norm1_g; n1.ada = w->ada; n1.temb = temb;
+  n1.rows = rows; n1.D = D; n1.shift_chunk = 0; n1.scale_chunk = 1; n1.eps = d->norm_eps;
+  if ((st = device_status(launch_norm_mod(n1, s), "norm1+modulation")) != DIT_OK) return st;
+
+  GemmArgs g{};
+  g.A = h; g.W = w->w_qkv; g.C = qkv; g.lda = D; g.ldw = D; g.ldc = 3 * D;
+  g.N = 3 * D; g.K = D; g.rows = rows; g.epilogue = EPI_STORE;
+  if ((st = device_status(launch_gemm(g, s), "qkv projection")) != DIT_OK) return st;
+
+  QkNormRopeArgs r{};
+  r.qkv = qkv; r.q_gain = w->q_g; r.k_gain = w->k_g; r.positions = l->positions; r.rows = rows;
+  r.heads = d->heads; r.head_dim = d->head_dim; r.row_stride = 3 * D; r.eps = d->qk_eps;
+  for (int i = 0; i < d->head_dim / 2; ++i)
+    r.inv_freq[i] = (float)std::pow((double)d->rope_base, -2.0 * i / (double)d->head_dim);
+  if ((st = device_status(launch_qk_norm_rope(r, s), "q/k norm+rope")) != DIT_OK) return st;
+
+  AttnArgs at{};
+  at.q = qkv; at.k = qkv + D; at.v = qkv + 2 * D; at.o = att;
+  at.batch_stride = (int64_t)L * 3 * D; at.row_stride = 3 * D;
+  at.o_batch_stride = (int64_t)L * D; at.o_row_stride = D;
+  at.batch = 1; at.seq_pad = L; at.heads = d->heads; at.head_dim = d->head_dim;
+  at.fixed_valid = attn_mode == DIT_ATTN_FIXED_VALID ? 1 : 0;
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+  at.valid[0] = rows.n_valid;
+  if ((st = device_status(launch_attention(at, s), "attention")) != DIT_OK) return st;
+
+  GemmArgs go{};
+  go.A = att; go.W = w->w_o; go.C = x1; go.lda = D; go.ldw = D; go.ldc = D; go.N = D; go.K = D;
+  go.rows = rows; go.epilogue = EPI_GATED_TO_F32; go.resid = x_in; go.ldr = D; go.ada = w->ada;
+  go.temb = temb; go.chunk = 2;
+  if ((st = device_status(launch_gemm(go, s), "out projection")) != DIT_OK) return st;
+
+  NormModArgs n2{};
+  n2.x = x1; n2.h = h2; n2.gain = w->norm2_g; n2.ada = w->ada; n2.temb = temb;
+  n2.rows = rows; n2.D = D; n2.shift_chunk = 3; n2.scale_chunk = 4; n2.eps = d->norm_eps;
+  n2.x_f32 = 1;
+  if ((st = device_status(launch_norm_mod(n2, s), "norm2+modulation")) != DIT_OK) return st;
+
+  GemmArgs gu{};
+  gu.A = h2; gu.W = w->w_gate_up; gu.C = act; gu.lda = D; gu.ldw = D; gu.ldc = m.ffn_ld;
+  gu.N = F; gu.K = D; gu.rows = rows; gu.epilogue = EPI_SWIGLU; gu.up_offset = F;
+  if ((st = device_status(launch_gemm(gu, s), "gate/up projection")) != DIT_OK) return st;
+
+  GemmArgs gd{};
+  gd.A = act; gd.W = w->w_down; gd.C = x_out; gd.lda = m.ffn_ld; gd.ldw = F; gd.ldc = D;
+  gd.N = D; gd.K = F; gd.rows = rows; gd.epilogue = EPI_GATED_F32_IN; gd.resid = x1; gd.ldr = D;
+  gd.ada = w->ada; gd.temb = temb; gd.chunk = 5;
+  if ((st = device_status(launch_gemm(gd, s), "down projection")) != DIT_OK) return st;
+  return DIT_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(DIT_ERR_INVALID, "workspace is null");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0)
+    return fail(DIT_ERR_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(DIT_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                need);
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_last_error(void) { return g_err.c_str(); }
+
+const char* dit_version(void) { return "avdit 0.1 (gfx950)"; }
+
+int dit_cache_schedule(const dit_cache_policy* policy, int32_t n_intervals, uint8_t* step_hit) {
+  g_err.clear();
+  int st = check_policy(policy);
+  if (st != DIT_OK) return st;
+  if (n_intervals < 0) return fail(DIT_ERR_INVALID, "n_intervals must be >= 0");
+  if (n_intervals > 0 && !step_hit) return fail(DIT_ERR_INVALID, "step_hit is null");
+  schedule(policy, n_intervals, step_hit);
+  return DIT_OK;
+}
+
+size_t dit_workspace_size(const dit_dims* dims, const dit_layout* layout, int32_t n_blocks,
+                          dit_workspace_map* map) {
+  g_err.clear();
+  if (check_dims(dims) != DIT_OK || check_layout(layout) != DIT_OK) return 0;
+  if (n_blocks < 0) {
+    fail(DIT_ERR_INVALID, "n_blocks must be >= 0");
+    return 0;
+  }
+  dit_workspace_map m;
+  build_map(dims, layout, n_blocks, &m);
+  if (map) *map = m;
+  return m.total;
+}
+
+int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
+                      const dit_block_weights* weights, const float* temb,
+                      const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st;
+  if ((st = check_dims(dims)) != DIT_OK) return st;
+  if ((st = check_layout(layout)) != DIT_OK) return st;
+  if ((st = check_weights(weights, 0)) != DIT_OK) return st;
+  if (!temb || !x_in || !x_out) return fail(DIT_ERR_INVALID, "temb, x_in and x_out must be non-null");
+  if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
+    return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
+  dit_workspace_map m;
+  build_map(dims, layout, 0, &m);
+  if ((st = check_ws(ws, ws_bytes, m.total)) != DIT_OK) return st;
+  const size_t act_bytes = (size_t)layout->seq_pad * dims->hidden * 2;
+  if (ranges_overlap(x_in, act_bytes, x_out, act_bytes) && act_bytes > 0)
+    return fail(DIT_ERR_INVALID, "x_in and x_out overlap");
+  if (act_bytes > 0 && (ranges_overlap(x_in, act_bytes, ws, m.total) ||
+                        ranges_overlap(x_out, act_bytes, ws, m.total)))
+    return fail(DIT_ERR_INVALID, "x_in or x_out overlaps the workspace");
+  if (layout->seq_pad == 0) return DIT_OK;
+  (void)hipGetLastError();
+  return enqueue_block(dims, layout, weights, temb, x_in, x_out, attn_mode,
+                       static_cast<char*>(ws), m, static_cast<hipStream_t>(stream));
+}
+
+int step_update(float* x, const uint16_t* v, uint16_t* x_bf16, const dit_layout* layout,
+                int32_t hidden, float dt_video, float dt_audio, void* stream) {
+  g_err.clear();
+  int st;
+  if ((st = check_layout(layout)) != DIT_OK) return st;
+  if (!x || !v) return fail(DIT_ERR_INVALID, "x and v must be non-null");
+  if (hidden <= 0 || (hidden & 7) != 0)
+    return fail(DIT_ERR_INVALID, "hidden %d must be a positive multiple of 8", hidden);
+  if (!std::isfinite(dt_video) || !std::isfinite(dt_audio))
+    return fail(DIT_ERR_INVALID, "step sizes must be finite");
+  if ((((uintptr_t)x) & 15) || (((uintptr_t)v) & 15) || (((uintptr_t)x_bf16) & 15))
+    return fail(DIT_ERR_INVALID, "x, v and x_bf16 must be 16-byte aligned");
+  avdit::StepArgs a{};
+  a.x = x; a.v = v; a.x_bf16 = x_bf16;
+  a.rows = avdit::RowLayout{layout->n_video, layout->n_video + layout->n_audio, layout->seq_pad};
+  a.D = hidden; a.dt_video = dt_video; a.dt_audio = dt_audio;
+  (void)hipGetLastError();
+  return device_status(avdit::launch_step_update(a, static_cast<hipStream_t>(stream)), "step update");
+}
+
+int denoise_loop(const dit_dims* dims, const dit_layout* layout,
+                 const dit_block_weights* blocks, int32_t n_blocks, int32_t n_intervals,
+                 const float* sigmas_video, const float* sigmas_audio,
+                 const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
+                 int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
+                 void* stream) {
+  g_err.clear();
+  int st;
+  if ((st = check_dims(dims)) != DIT_OK) return st;
+  if ((st = check_layout(layout)) != DIT_OK) return st;
+  if ((st = check_policy(policy)) != DIT_OK) return st;
+  if (n_blocks < 1) return fail(DIT_ERR_INVALID, "n_blocks must be >= 1");
+  if (!blocks) return fail(DIT_ERR_INVALID, "blocks is null");
+  for (int b = 0; b < n_blocks; ++b)
+    if ((st = check_weights(&blocks[b], b)) != DIT_OK) return st;
+  if (n_intervals < 0) return fail(DIT_ERR_INVALID, "n_intervals must be >= 0");
+  if (n_intervals > 0 && (!sigmas_video || !sigmas_audio || !temb_steps))
+    return fail(DIT_ERR_INVALID, "sigmas and temb_steps must be non-null");
+  if (!x_latent) return fail(DIT_ERR_INVALID, "x_latent is null");
+  if (((uintptr_t)x_latent) & 15) return fail(DIT_ERR_INVALID, "x_latent must be 16-byte aligned");
+  if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
+    return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
+  for (int i = 0; i <= n_intervals && n_intervals > 0; ++i)
+    if (!std::isfinite(sigmas_video[i]) || !std::isfinite(sigmas_audio[i]))
+      return fail(DIT_ERR_INVALID, "sigma %d is not finite", i);
+  dit_workspace_map m;
+  build_map(dims, layout, n_blocks, &m);
+  if ((st = check_ws(ws, ws_bytes, m.total)) != DIT_OK) return st;
+  const size_t lat_bytes = (size_t)layout->seq_pad * dims->hidden * 4;
+  if (lat_bytes > 0 && ranges_overlap(x_latent, lat_bytes, ws, m.total))
+    return fail(DIT_ERR_INVALID, "x_latent overlaps the workspace");
+
+  // Request-scoped cache state: the schedule and the retained velocity live only here.
+  std::vector<uint8_t> hits((size_t)n_intervals);
+  schedule(policy, n_intervals, hits.data());
+  int32_t n_hits = 0;
+  for (uint8_t h : hits) n_hits += h;
+
+  if (layout->seq_pad > 0 && n_intervals > 0) {
+    (void)hipGetLastError();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(ws);
+    uint16_t* x_bf16 = reinterpret_cast<uint16_t*>(base + m.x_bf16);
+    uint16_t* vel = reinterpret_cast<uint16_t*>(base + m.velocity);
+    uint16_t* pp[2] = {reinterpret_cast<uint16_t*>(base + m.ping),
+                       reinterpret_cast<uint16_t*>(base + m.pong)};
+    const avdit::RowLayout rows{layout->n_video, layout->n_video + layout->n_audio, layout->seq_pad};
+    const size_t temb_step = (size_t)dims->n_mod * 6 * dims->hidden;
+
+    avdit::StepArgs first{};
+    first.x = x_latent; first.v = nullptr; first.x_bf16 = x_bf16; first.rows = rows;
+    first.D = dims->hidden;
+    if ((st = device_status(avdit::launch_step_update(first, s), "latent conversion")) != DIT_OK)
+      return st;
+    for (int32_t i = 0; i < n_intervals; ++i) {
+      if (!hits[i]) {
+        const float* temb_i = temb_steps + (size_t)i * temb_step;
+        for (int32_t b = 0; b < n_blocks; ++b) {
+          const uint16_t* in = b == 0 ? x_bf16 : pp[(b - 1) & 1];
+          uint16_t* out = b == n_blocks - 1 ? vel : pp[b & 1];
+          if ((st = enqueue_block(dims, layout, &blocks[b], temb_i, in, out, attn_mode, base, m, s)) !=
+              DIT_OK)
+            return st;
+        }
+      }
+      avdit::StepArgs a{};
+      a.x = x_latent; a.v = vel; a.x_bf16 = (i + 1 < n_intervals) ? x_bf16 : nullptr;
+      a.rows = rows; a.D = dims->hidden;
+      a.dt_video = sigmas_video[i + 1] - sigmas_video[i];
+      a.dt_audio = sigmas_audio[i + 1] - sigmas_audio[i];
+      if ((st = device_status(avdit::launch_step_update(a, s), "step update")) != DIT_OK) return st;
+    }
+  }
+  if (stats) {
+    const int32_t calls = n_intervals - n_hits;
+    const double V = (double)layout->n_video + layout->n_audio;
+    const double D = dims->hidden, F = dims->ffn;
+    stats->dit_calls = calls;
+    stats->cache_hits = n_hits;
+    stats->executed_blocks = (int64_t)calls * n_blocks;
+    stats->skipped_blocks = (int64_t)n_hits * n_blocks;
+    stats->useful_flops = (double)calls * n_blocks * (8 * V * D * D + 6 * V * D * F + 4 * V * V * D);
+    if (stats->step_hit && n_intervals > 0) std::memcpy(stats->step_hit, hits.data(), hits.size());
+  }
+  return DIT_OK;
+}
+
+int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                          int32_t batch, int32_t seq_pad, int32_t heads, int32_t head_dim,
+                          int64_t batch_stride, int64_t row_stride, int64_t o_batch_stride,
+                          int64_t o_row_stride, const int32_t* valid_lens, int32_t attn_mode,
+                          void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !o || !valid_lens) return fail(DIT_ERR_INVALID, "null pointer argument");
+  if (batch < 1 || batch > avdit::ATTN_MAX_BATCH)
+    return fail(DIT_ERR_INVALID, "batch %d outside [1, %d]", batch, (int)avdit::ATTN_MAX_BATCH);
+  if (seq_pad < 0 || seq_pad > kMaxSeq) return fail(DIT_ERR_INVALID, "seq_pad %d out of range", seq_pad);
+  if (heads < 1) return fail(DIT_ERR_INVALID, "heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+  const int64_t width = (int64_t)heads * head_dim;
+  if (row_stride < width || o_row_stride < width || (row_stride & 7) || (o_row_stride & 7))
+    return fail(DIT_ERR_INVALID, "row strides must be >= heads*head_dim and multiples of 8");
+  if (batch > 1 && (batch_stride < (int64_t)seq_pad * row_stride ||
+                    o_batch_stride < (int64_t)seq_pad * o_row_stride))
+    return fail(DIT_ERR_INVALID, "batch strides must cover seq_pad rows");
+  if ((batch_stride & 7) || (o_batch_stride & 7))
+    return fail(DIT_ERR_INVALID, "batch strides must be multiples of 8");
+  if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)o)) & 15)
+    return fail(DIT_ERR_INVALID, "q, k, v and o must be 16-byte aligned");
+  if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
+    return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
+  avdit::AttnArgs a{};
+  for (int b = 0; b < batch; ++b) {
+    if (valid_lens[b] < 0 || valid_lens[b] > seq_pad)
+      return fail(DIT_ERR_INVALID, "valid_lens[%d] = %d outside [0, %d]", b, valid_lens[b], seq_pad);
+    a.valid[b] = valid_lens[b];
+  }
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.batch_stride = batch_stride; a.row_stride = row_stride;
+  a.o_batch_stride = o_batch_stride; a.o_row_stride = o_row_stride;
+  a.batch = batch; a.seq_pad = seq_pad; a.heads = heads; a.head_dim = head_dim;
+  a.fixed_valid = attn_mode == DIT_ATTN_FIXED_VALID ? 1 : 0;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  (void)hipGetLastError();
+  return device_status(avdit::launch_attention(a, static_cast<hipStream_t>(stream)), "attention");
+}
+
+}  // extern "C"

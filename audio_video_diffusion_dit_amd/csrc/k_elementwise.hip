@@ -1,0 +1,295 @@
+// HBM-bound kernels of the block and the loop: RMSNorm + indexed AdaLN modulation,
+// per-head Q/K RMSNorm + NeoX RoPE, and the per-modality Euler update.
+//
+// Each is a single pass with 16-byte coalesced accesses and wavefront (or lane-group)
+// reductions; all arithmetic is fp32 and every stored bf16 is rounded once.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace avdit {
+
+// ---------------------------------------------------------------------------------------
+// RMSNorm fused with indexed AdaLN modulation (TeleFuser PR #38, section 2; TeleFuser PR #23,
+// "Changes Made": indexed modulation). The input is the bf16 block input (norm1) or the fp32
+// mid-block residual (norm2). One wave owns a run of ROWS_PER_WAVE consecutive
+// rows; the modulation of the current modality, folded to mul = g * (1 + scale) and
+// add = shift, stays in registers and is reloaded only when the run crosses the
+// video/audio boundary, so the tables cost almost no cache traffic per row.
+// ---------------------------------------------------------------------------------------
+constexpr int kNormRowsPerWave = 8;
+
+template <int CPL, bool F32IN>  // CPL: 8-element chunks per lane, ceil(D / 512)
+__global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int D = a.D;
+  const int nchunk = D >> 3;
+  const float inv_d = 1.0f / (float)D;
+  float mul[CPL][8];
+  float add[CPL][8];
+  int cur = -1;
+
+  for (int rr = 0; rr < kNormRowsPerWave; ++rr) {
+    const int row = wave * kNormRowsPerWave + rr;
+    if (row >= a.rows.seq_pad) return;
+    uint4* out = reinterpret_cast<uint4*>(a.h + (size_t)row * D);
+    if (row >= a.rows.n_valid) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunk) out[c] = zero4();
+      }
+      continue;
+    }
+    const int m = row < a.rows.n_video ? 0 : 1;
+    if (m != cur) {
+      cur = m;
+      const float* A = a.ada + (size_t)m * 6 * D;
+      const float* T = a.temb + (size_t)m * 6 * D;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunk) {
+          const int d0 = c * 8;
+#pragma unroll
+          for (int e = 0; e < 8; e += 4) {
+            const float4 g = *reinterpret_cast<const float4*>(a.gain + d0 + e);
+            const float4 sa = *reinterpret_cast<const float4*>(A + a.scale_chunk * D + d0 + e);
+            const float4 st = *reinterpret_cast<const float4*>(T + a.scale_chunk * D + d0 + e);
+            const float4 ha = *reinterpret_cast<const float4*>(A + a.shift_chunk * D + d0 + e);
+            const float4 ht = *reinterpret_cast<const float4*>(T + a.shift_chunk * D + d0 + e);
+            mul[i][e + 0] = g.x * (1.0f + (sa.x + st.x));
+            mul[i][e + 1] = g.y * (1.0f + (sa.y + st.y));
+            mul[i][e + 2] = g.z * (1.0f + (sa.z + st.z));
+            mul[i][e + 3] = g.w * (1.0f + (sa.w + st.w));
+            add[i][e + 0] = ha.x + ht.x;
+            add[i][e + 1] = ha.y + ht.y;
+            add[i][e + 2] = ha.z + ht.z;
+            add[i][e + 3] = ha.w + ht.w;
+          }
+        }
+      }
+    }
+    // 8 elements per chunk, held as fp32
+    float xv[CPL][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      if (F32IN) {
+        const float4* in = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)row * D);
+        const float4 p0 = c < nchunk ? in[2 * c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 p1 = c < nchunk ? in[2 * c + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[i][0] = p0.x; xv[i][1] = p0.y; xv[i][2] = p0.z; xv[i][3] = p0.w;
+        xv[i][4] = p1.x; xv[i][5] = p1.y; xv[i][6] = p1.z; xv[i][7] = p1.w;
+      } else {
+        const uint4* in = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)row * D);
+        const uint4 v = c < nchunk ? in[c] : zero4();
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xv[i][2 * j] = bf_lo(w[j]);
+          xv[i][2 * j + 1] = bf_hi(w[j]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(xv[i][e], xv[i][e], ss);
+    }
+    ss = wave_sum(ss);
+    const float r = rsqrtf(ss * inv_d + a.eps);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) {
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y0 = fmaf(xv[i][2 * j] * r, mul[i][2 * j], add[i][2 * j]);
+          const float y1 = fmaf(xv[i][2 * j + 1] * r, mul[i][2 * j + 1], add[i][2 * j + 1]);
+          o[j] = pack_bf16x2(y0, y1);
+        }
+        out[c] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+}
+
+template <int CPL>
+static hipError_t norm_mod_instance(const NormModArgs& a, hipStream_t s) {
+  const int waves = (a.rows.seq_pad + kNormRowsPerWave - 1) / kNormRowsPerWave;
+  const int blocks = (waves + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  if (a.x_f32)
+    hipLaunchKernelGGL((k_norm_mod<CPL, true>), dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_norm_mod<CPL, false>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_mod(const NormModArgs& a, hipStream_t s) {
+  if (a.D <= 0 || (a.D & 7) != 0) return hipErrorInvalidValue;
+  const int cpl = (a.D / 8 + 63) / 64;
+  if (cpl <= 1) return norm_mod_instance<1>(a, s);
+  if (cpl <= 2) return norm_mod_instance<2>(a, s);
+  if (cpl <= 4) return norm_mod_instance<4>(a, s);
+  if (cpl <= 6) return norm_mod_instance<6>(a, s);
+  if (cpl <= 8) return norm_mod_instance<8>(a, s);
+  if (cpl <= 12) return norm_mod_instance<12>(a, s);
+  if (cpl <= 16) return norm_mod_instance<16>(a, s);
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------------------
+// Per-head Q/K RMSNorm + NeoX rotary embedding (TeleFuser PR #38, section 2; TeleFuser
+// PR #23, "Changes Made"). A group of head_dim/8 lanes owns one token: lane j holds
+// elements 8j..8j+7 of a head vector, so the rotate-half partner of lane j is lane
+// j ^ (group/2). The token's rotation angles are computed once (one sincos per element
+// slot) and reused for all 2H vectors (q heads then k heads, contiguous in qkv).
+// ---------------------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
+  constexpr int G = DH / 8;         // lanes per head vector
+  constexpr int HALF_G = G / 2;
+  constexpr int TPB = 256 / G;      // tokens per block
+  const int gl = threadIdx.x % G;
+  const int token = blockIdx.x * TPB + threadIdx.x / G;
+  if (token >= a.rows.n_valid) return;
+
+  const float pos = a.positions ? (float)a.positions[token] : (float)token;
+  const int gg = gl % HALF_G;       // frequency block of this lane: i = 8 * gg + e
+  float inv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inv[e] = 0.0f;
+#pragma unroll
+  for (int b = 0; b < HALF_G; ++b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) inv[e] = (gg == b) ? a.inv_freq[8 * b + e] : inv[e];
+  }
+  float cs[8], sn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sincosf(pos * inv[e], &sn[e], &cs[e]);
+
+  float gq[8], gk[8];
+#pragma unroll
+  for (int e = 0; e < 8; e += 4) {
+    const float4 q4 = *reinterpret_cast<const float4*>(a.q_gain + gl * 8 + e);
+    const float4 k4 = *reinterpret_cast<const float4*>(a.k_gain + gl * 8 + e);
+    gq[e] = q4.x; gq[e + 1] = q4.y; gq[e + 2] = q4.z; gq[e + 3] = q4.w;
+    gk[e] = k4.x; gk[e + 1] = k4.y; gk[e + 2] = k4.z; gk[e + 3] = k4.w;
+  }
+  const bool first_half = gl < HALF_G;
+  const float inv_dh = 1.0f / (float)DH;
+  uint16_t* base = a.qkv + (size_t)token * a.row_stride + gl * 8;
+  const int nvec = 2 * a.heads;
+
+  constexpr int U = 4;
+  for (int v0 = 0; v0 < nvec; v0 += U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      raw[u] = (v0 + u < nvec) ? *reinterpret_cast<const uint4*>(base + (size_t)(v0 + u) * DH)
+                               : zero4();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int vec = v0 + u;
+      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf_lo(w[j]);
+        x[2 * j + 1] = bf_hi(w[j]);
+      }
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+      ss = group_sum<G>(ss);
+      const float r = rsqrtf(ss * inv_dh + a.eps);
+      const bool is_q = vec < a.heads;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[e] * r * (is_q ? gq[e] : gk[e]);
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __shfl_xor(y[e], HALF_G, 64);
+        const float p1 = __shfl_xor(y[e + 1], HALF_G, 64);
+        const float r0 = first_half ? fmaf(y[e], cs[e], -p0 * sn[e]) : fmaf(y[e], cs[e], p0 * sn[e]);
+        const float r1 = first_half ? fmaf(y[e + 1], cs[e + 1], -p1 * sn[e + 1])
+                                    : fmaf(y[e + 1], cs[e + 1], p1 * sn[e + 1]);
+        o[e / 2] = pack_bf16x2(r0, r1);
+      }
+      if (vec < nvec)
+        *reinterpret_cast<uint4*>(base + (size_t)vec * DH) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s) {
+  if ((a.row_stride & 7) != 0) return hipErrorInvalidValue;
+  const int n = a.rows.n_valid;
+  if (n <= 0) return hipSuccess;
+  if (a.head_dim == 128) {
+    const int tpb = 256 / 16;
+    hipLaunchKernelGGL(k_qk_norm_rope<128>, dim3((n + tpb - 1) / tpb), dim3(256), 0, s, a);
+  } else if (a.head_dim == 64) {
+    const int tpb = 256 / 8;
+    hipLaunchKernelGGL(k_qk_norm_rope<64>, dim3((n + tpb - 1) / tpb), dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Flow-matching Euler update with per-modality step sizes (TeleFuser PR #23, "Motivation"
+// and "Changes Made": independent video/audio schedulers, optimized scheduler updates).
+// One thread per 8 consecutive elements of a row; the bf16 copy is the next DiT input.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_step_update(StepArgs a) {
+  const int per_row = a.D >> 3;
+  const long total = (long)a.rows.seq_pad * per_row;
+  for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (long)gridDim.x * 256) {
+    const int row = (int)(idx / per_row);
+    const int c = (int)(idx - (long)row * per_row);
+    float4* xp = reinterpret_cast<float4*>(a.x + (size_t)row * a.D + 8 * c);
+    uint4* bp = a.x_bf16 ? reinterpret_cast<uint4*>(a.x_bf16 + (size_t)row * a.D + 8 * c)
+                         : nullptr;
+    if (row >= a.rows.n_valid) {
+      xp[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      xp[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bp) *bp = zero4();
+      continue;
+    }
+    float4 x0 = xp[0], x1 = xp[1];
+    if (a.v) {
+      const float dt = row < a.rows.n_video ? a.dt_video : a.dt_audio;
+      const uint4 vv = *reinterpret_cast<const uint4*>(a.v + (size_t)row * a.D + 8 * c);
+      x0.x = fmaf(dt, bf_lo(vv.x), x0.x);
+      x0.y = fmaf(dt, bf_hi(vv.x), x0.y);
+      x0.z = fmaf(dt, bf_lo(vv.y), x0.z);
+      x0.w = fmaf(dt, bf_hi(vv.y), x0.w);
+      x1.x = fmaf(dt, bf_lo(vv.z), x1.x);
+      x1.y = fmaf(dt, bf_hi(vv.z), x1.y);
+      x1.z = fmaf(dt, bf_lo(vv.w), x1.z);
+      x1.w = fmaf(dt, bf_hi(vv.w), x1.w);
+      xp[0] = x0;
+      xp[1] = x1;
+    }
+    if (bp)
+      *bp = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                       pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+  }
+}
+
+hipError_t launch_step_update(const StepArgs& a, hipStream_t s) {
+  if (a.D <= 0 || (a.D & 7) != 0) return hipErrorInvalidValue;
+  const long total = (long)a.rows.seq_pad * (a.D >> 3);
+  if (total == 0) return hipSuccess;
+  long blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_step_update, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace avdit

@@ -1,0 +1,281 @@
+// bf16 MFMA GEMM for the block's projections: C[m][n] = sum_k A[m][k] * W[n][k], both operands
+// contiguous along k (activations [tokens, K], weights [out, in]), fp32 accumulation, with the
+// epilogue fused: plain store (QKV), gated residual (out-projection into the fp32 mid-block residual, down-projection from it), or
+// SwiGLU over interleaved gate/up weight rows (gate/up projection, TeleFuser PR #23, "Changes
+// Made": fused SwiGLU).
+//
+// Design for gfx950:
+//  * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (BN/2 features) x (BM/2 tokens)
+//    accumulator block made of 32x32 tiles of v_mfma_f32_32x32x16_bf16. The weight tile is the
+//    MFMA A operand and the token tile the B operand, so every lane ends up holding 4
+//    consecutive output features of one token: epilogue loads/stores are 8-byte vectors.
+//  * k-tiles of 64 staged through LDS, double buffered, one barrier per k-tile; the next tile's
+//    global loads are in flight while the current one is multiplied. LDS rows are 128 bytes with
+//    the 16-byte chunk index XOR-swizzled by (row & 7), which keeps both the 16-byte fragment
+//    reads (32 rows, same chunk) and the loader's writes free of bank conflicts.
+//  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
+//    receives a contiguous range of tiles, and tiles are ordered in groups of 8 token-tiles,
+//    so the workgroups resident on one XCD share both operand panels in that XCD's L2.
+//  * Rows at or beyond n_valid are never multiplied: their loads are predicated to zero and a
+//    tile that lies entirely in the tail only writes zeros (the zero-tail merge of TeleFuser
+//    PR #38, section 2).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace avdit {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBK = 64;  // k-tile; 8 chunks of 8 bf16 per LDS row
+
+template <bool ALIGNED>
+__device__ __forceinline__ u32x4 load_chunk(const uint16_t* __restrict__ base, int64_t ld,
+                                            int row, bool row_ok, int k, int K) {
+  if (!row_ok || k >= K) return u32x4{0u, 0u, 0u, 0u};
+  const uint16_t* p = base + (int64_t)row * ld + k;
+  if (ALIGNED) return *reinterpret_cast<const u32x4*>(p);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = (k + 2 * j < K) ? p[2 * j] : 0u;
+    const uint32_t hi = (k + 2 * j + 1 < K) ? p[2 * j + 1] : 0u;
+    w[j] = lo | (hi << 16);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+template <int BM, int BN, int EPI, bool ALIGNED>
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int TM = BM / 2;          // tokens per wave
+  constexpr int TN = BN / 2;          // weight rows per wave
+  constexpr int MT = TM / 32;         // 32-token sub-tiles per wave
+  constexpr int FT = TN / 32;         // 32-row weight sub-tiles per wave
+  constexpr int ROWS = BM + BN;       // LDS rows per stage (weights first)
+  constexpr int PT = ROWS * 8 / 256;  // 16-byte chunks each thread stages per k-tile
+  static_assert(EPI != EPI_SWIGLU || (FT % 2) == 0, "SwiGLU pairs gate/up sub-tiles");
+
+  __shared__ u32x4 lds[2][ROWS * 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;   // token half
+  const int wn = wave >> 1;  // feature half
+
+  // ---- tile selection: XCD-contiguous ranges, grouped token-tile order ----
+  const int nt = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = nt >> 3, rem = nt & 7;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+  constexpr int GM = 8;
+  const int group = logical / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int in_group = logical - group * GM * tiles_n;
+  const int tile_m = first_m + in_group % gm;
+  const int tile_n = in_group / gm;
+
+  const int m0 = tile_m * BM;
+  const int n_valid = a.rows.n_valid;
+  const int seq_pad = a.rows.seq_pad;
+  // first output feature of this tile (SwiGLU tiles cover BN/2 outputs)
+  const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
+
+  f32x16 acc[FT][MT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.0f;
+
+  if (m0 < n_valid) {
+    // ---- staging map: chunk q = tid + 256 i -> LDS row q / 8, chunk q % 8 ----
+    const int ck = tid & 7;
+    int src_row[PT];
+    bool src_ok[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      if (r < BN) {
+        int wrow, feat;
+        if (EPI == EPI_SWIGLU) {
+          const int blk = r >> 5;
+          feat = n0 + (blk >> 1) * 32 + (r & 31);
+          wrow = (blk & 1) ? a.up_offset + feat : feat;
+        } else {
+          feat = n0 + r;
+          wrow = feat;
+        }
+        src_row[i] = wrow;
+        src_ok[i] = feat < a.N;
+      } else {
+        const int tok = m0 + (r - BN);
+        src_row[i] = tok;
+        src_ok[i] = tok < n_valid;
+      }
+    }
+    const int nk = (a.K + kBK - 1) / kBK;
+    u32x4 stage[PT];
+    auto load_stage = [&](int kt) {
+      const int k = kt * kBK + ck * 8;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        stage[i] = (r < BN) ? load_chunk<ALIGNED>(a.W, a.ldw, src_row[i], src_ok[i], k, a.K)
+                            : load_chunk<ALIGNED>(a.A, a.lda, src_row[i], src_ok[i], k, a.K);
+      }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        lds[buf][r * 8 + (ck ^ (r & 7))] = stage[i];
+      }
+    };
+
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load_stage(kt + 1);
+      const u32x4* L = lds[cur];
+#pragma unroll
+      for (int s = 0; s < kBK / 16; ++s) {
+        const int c = 2 * s + hh;
+        bf16x8 af[FT], bf[MT];
+#pragma unroll
+        for (int f = 0; f < FT; ++f) {
+          const int r = wn * TN + f * 32 + l32;
+          af[f] = __builtin_bit_cast(bf16x8, L[r * 8 + (c ^ (r & 7))]);
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int r = BN + wm * TM + t * 32 + l32;
+          bf[t] = __builtin_bit_cast(bf16x8, L[r * 8 + (c ^ (r & 7))]);
+        }
+#pragma unroll
+        for (int f = 0; f < FT; ++f)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f], bf[t], acc[f][t], 0, 0, 0);
+      }
+      if (kt + 1 < nk) store_stage(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds features fb..fb+3 of token `tok` for each (f, t, j) ----
+  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int tok = m0 + wm * TM + t * 32 + l32;
+    if (tok >= seq_pad) continue;
+    const bool valid = tok < n_valid;
+    const int mod = tok < a.rows.n_video ? 0 : 1;
+    constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
+#pragma unroll
+    for (int f = 0; f < OUT_T; ++f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int fb = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
+        if (fb >= a.N) continue;
+        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (valid) {
+          if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              o[i] = silu_mul(acc[2 * f][t][4 * j + i], acc[2 * f + 1][t][4 * j + i]);
+          } else if constexpr (GATED) {
+            float r[4];
+            if constexpr (EPI == EPI_GATED_TO_F32) {
+              const u32x2 rr = *reinterpret_cast<const u32x2*>(
+                  static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fb);
+              r[0] = bf_lo(rr.x); r[1] = bf_hi(rr.x); r[2] = bf_lo(rr.y); r[3] = bf_hi(rr.y);
+            } else {
+              const float4 rr = *reinterpret_cast<const float4*>(
+                  static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
+              r[0] = rr.x; r[1] = rr.y; r[2] = rr.z; r[3] = rr.w;
+            }
+            const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
+            const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
+            const float4 gt = *reinterpret_cast<const float4*>(a.temb + goff);
+            o[0] = fmaf(ga.x + gt.x, acc[f][t][4 * j + 0], r[0]);
+            o[1] = fmaf(ga.y + gt.y, acc[f][t][4 * j + 1], r[1]);
+            o[2] = fmaf(ga.z + gt.z, acc[f][t][4 * j + 2], r[2]);
+            o[3] = fmaf(ga.w + gt.w, acc[f][t][4 * j + 3], r[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
+          }
+        }
+        if constexpr (EPI == EPI_GATED_TO_F32) {
+          float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
+          *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
+          if (fb + 4 <= a.N) {
+            *reinterpret_cast<u32x2*>(crow + fb) =
+                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (fb + i < a.N) crow[fb + i] = to_bf16(o[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int EPI, bool ALIGNED>
+static hipError_t gemm_instance(const GemmArgs& a, hipStream_t s) {
+  const int out_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int tiles_m = (a.rows.seq_pad + BM - 1) / BM;
+  const int tiles_n = (a.N + out_per_tile - 1) / out_per_tile;
+  const int nt = tiles_m * tiles_n;
+  if (nt == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm<BM, BN, EPI, ALIGNED>), dim3(nt), dim3(256), 0, s, a, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool ALIGNED>
+static hipError_t gemm_dispatch_epi(const GemmArgs& a, hipStream_t s) {
+  switch (a.epilogue) {
+    case EPI_STORE: return gemm_instance<BM, BN, EPI_STORE, ALIGNED>(a, s);
+    case EPI_GATED_TO_F32: return gemm_instance<BM, BN, EPI_GATED_TO_F32, ALIGNED>(a, s);
+    case EPI_GATED_F32_IN: return gemm_instance<BM, BN, EPI_GATED_F32_IN, ALIGNED>(a, s);
+    case EPI_SWIGLU: return gemm_instance<BM, BN, EPI_SWIGLU, ALIGNED>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.N <= 0 || a.K <= 0) return hipErrorInvalidValue;
+  // Epilogue vectors are 4 features wide and 8-byte aligned.
+  if ((a.ldc & 3) != 0) return hipErrorInvalidValue;
+  const bool gated = a.epilogue == EPI_GATED_TO_F32 || a.epilogue == EPI_GATED_F32_IN;
+  if (gated && ((a.N & 3) != 0 || (a.ldr & 3) != 0)) return hipErrorInvalidValue;
+  const bool aligned = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&
+                       ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
+                       ((reinterpret_cast<uintptr_t>(a.W) & 15) == 0);
+  const int out_big = (a.epilogue == EPI_SWIGLU) ? 128 : 256;
+  const long tiles_big = (long)((a.rows.n_valid + 255) / 256) * ((a.N + out_big - 1) / out_big);
+  const bool big = tiles_big >= 512;
+  if (aligned) {
+    return big ? gemm_dispatch_epi<256, 256, true>(a, s) : gemm_dispatch_epi<128, 128, true>(a, s);
+  }
+  return gemm_dispatch_epi<128, 128, false>(a, s);
+}
+
+}  // namespace avdit

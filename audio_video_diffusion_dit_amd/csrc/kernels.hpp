@@ -1,0 +1,99 @@
+// Launch interfaces of the gfx950 kernels. Host code fills these argument structs after
+// validating shapes; each launcher checks the structural preconditions its kernel relies on
+// (alignment, tile coverage) and returns hipErrorInvalidValue instead of launching if one
+// fails, so a kernel never sees a shape it was not written for.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace avdit {
+
+// Rows of the packed sequence: [0, n_video) video, [n_video, n_valid) audio, then the tail.
+struct RowLayout {
+  int32_t n_video;
+  int32_t n_valid;
+  int32_t seq_pad;
+};
+
+// h = RMSNorm(x) * g * (1 + E[m][scale_chunk]) + E[m][shift_chunk], E = ada + temb.
+struct NormModArgs {
+  const void* x;      // [seq_pad, D] bf16, or fp32 when x_f32
+  uint16_t* h;        // [seq_pad, D] bf16
+  const float* gain;  // [D]
+  const float* ada;   // [2, 6, D]
+  const float* temb;  // [2, 6, D]
+  RowLayout rows;
+  int32_t D;
+  int32_t shift_chunk, scale_chunk;
+  float eps;
+  int32_t x_f32;      // 1: x is fp32
+};
+hipError_t launch_norm_mod(const NormModArgs& a, hipStream_t s);
+
+// Per-head RMSNorm + NeoX RoPE of the q and k column blocks of qkv [seq_pad, 3D], in place.
+struct QkNormRopeArgs {
+  uint16_t* qkv;
+  const float* q_gain;     // [Dh]
+  const float* k_gain;     // [Dh]
+  const int32_t* positions;  // [seq_pad] or null (position = row)
+  RowLayout rows;
+  int32_t heads, head_dim;
+  int64_t row_stride;      // elements between rows (3D)
+  float eps;
+  float inv_freq[64];      // base^(-2i/Dh), i < Dh/2, rounded once from float64
+};
+hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s);
+
+// x += dt_m * v (skipped when v is null), x_bf16 = bf16(x); tail rows of both set to 0.
+struct StepArgs {
+  float* x;
+  const uint16_t* v;
+  uint16_t* x_bf16;
+  RowLayout rows;
+  int32_t D;
+  float dt_video, dt_audio;
+};
+hipError_t launch_step_update(const StepArgs& a, hipStream_t s);
+
+// C[m][n] = sum_k A[m][k] * W[n][k] with a fused epilogue.
+enum GemmEpilogue : int32_t {
+  EPI_STORE = 0,        // out (bf16) = acc
+  EPI_GATED_TO_F32 = 1, // out (fp32) = resid (bf16) + (ada + temb)[mod(m)][chunk][n] * acc
+  EPI_SWIGLU = 2,       // out (bf16) = silu(acc_gate) * acc_up, gate row n, up row up_offset + n
+  EPI_GATED_F32_IN = 3, // out (bf16) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
+};
+struct GemmArgs {
+  const uint16_t* A;  // [rows, K] activations, row stride lda
+  const uint16_t* W;  // [N_w, K] weights, row stride ldw
+  void* C;            // [rows, N] output (bf16, or fp32 for EPI_GATED_TO_F32), row stride ldc
+  int64_t lda, ldw, ldc;
+  int32_t N, K;       // output features, reduction length
+  RowLayout rows;     // rows >= n_valid of C are written 0; rows >= seq_pad untouched
+  int32_t epilogue;
+  const void* resid;      // gated epilogues: [rows, N] (bf16 or fp32), row stride ldr
+  int64_t ldr;
+  const float* ada;       // gated epilogues: [2, 6, N]
+  const float* temb;      // gated epilogues: [2, 6, N]
+  int32_t chunk;          // gated epilogues: modulation chunk of the gate
+  int32_t up_offset;      // EPI_SWIGLU: first up row of W (= F)
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// Flash-style attention over packed requests; element (b, i, h, d) of q/k/v at
+// b * batch_stride + i * row_stride + h * head_dim + d.
+enum { ATTN_MAX_BATCH = 64 };
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int64_t batch_stride, row_stride, o_batch_stride, o_row_stride;
+  int32_t batch, seq_pad, heads, head_dim;
+  int32_t fixed_valid;  // 1: sweep the whole padded length with a key mask
+  float scale_log2;     // log2(e) / sqrt(head_dim)
+  int32_t valid[ATTN_MAX_BATCH];
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace avdit

@@ -1,0 +1,200 @@
+/*
+ * avdit.h -- C-ABI of the MI355X (gfx950) joint audio-video DiT denoising step.
+ *
+ * Pages cited (by title and section):
+ *   [P1] TeleFuser PR #38, "perf(minimax-h3): add conservative DiT velocity reuse"
+ *   [P2] 1Cat-vLLM PR #584, "[Video] Add native H3 request-scoped TeaCache and Cache-DiT"
+ *   [P3] TeleFuser PR #23, "[FEAT] Add MiniMax H3 joint audio-video generation"
+ *
+ * Conventions shared by every entry point:
+ *  - "dev" pointers are HIP device memory, "host" pointers are ordinary CPU memory.
+ *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, round-to-nearest-even
+ *    on every store). All math inside the kernels is fp32.
+ *  - Tensors are row-major and token-major. Weights use the [out, in] layout, so both
+ *    operands of every projection are contiguous along the reduction axis.
+ *  - The packed sequence has seq_pad rows: video rows 0..n_video-1 (modality 0), audio
+ *    rows n_video..n_valid-1 (modality 1), then a tail up to seq_pad ([P3] "Motivation",
+ *    packed joint token layout; [P1] section 2, zero tail). Every output tensor has an
+ *    exactly-zero tail, whatever the input tail holds.
+ *  - Ownership: the caller allocates and owns every buffer, the workspace and the
+ *    stream. The library allocates no device memory and keeps no state between calls
+ *    except a thread-local error string. Device work is enqueued asynchronously on the
+ *    given stream (NULL = the default stream); calls return after enqueueing.
+ *  - Errors: every argument is validated before anything is enqueued. On failure
+ *    nothing is enqueued, a negative status is returned and dit_last_error() describes
+ *    it. A launch failure reported by the runtime after enqueueing maps to
+ *    DIT_ERR_DEVICE. There are no environment variables and no fallback paths.
+ */
+#ifndef AVDIT_H
+#define AVDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DIT_OK = 0,
+  DIT_ERR_INVALID = -1,      /* a null pointer, inconsistent sizes or out-of-range values */
+  DIT_ERR_UNSUPPORTED = -2,  /* a well-formed request this library does not implement */
+  DIT_ERR_WORKSPACE = -3,    /* the workspace is smaller than dit_workspace_size() */
+  DIT_ERR_DEVICE = -4        /* the HIP runtime rejected a launch */
+};
+
+enum { DIT_ATTN_VALID_ONLY = 0, DIT_ATTN_FIXED_VALID = 1 };
+enum { DIT_CACHE_OFF = 0, DIT_CACHE_VELOCITY = 1 };
+
+/* Model dimensions. hidden = heads * head_dim; head_dim is 64 or 128; n_mod is 2 (video,
+ * audio). norm_eps is the RMSNorm epsilon of the token norms, qk_eps that of the per-head
+ * Q/K norms, rope_base the NeoX rotary base. */
+typedef struct {
+  int32_t hidden, heads, head_dim, ffn, n_mod;
+  float norm_eps, qk_eps, rope_base;
+} dit_dims;
+
+/* Packed-sequence layout ([P3] "Motivation"; [P1] section 2). positions: dev int32
+ * [seq_pad] rotary positions, or NULL for position(l) = l. Request-static: built once per
+ * request and reused by every block and every step ([P3] "Changes Made"). */
+typedef struct {
+  int32_t n_video, n_audio, seq_pad;
+  const int32_t* positions;
+} dit_layout;
+
+/* One block's parameters (all dev). Matrices are bf16, the rest fp32 (precision-sensitive
+ * parameters stay fp32, [P3] "Motivation").
+ *   w_qkv [3D, D]: rows 0..D-1 produce q, D..2D-1 k, 2D..3D-1 v; inside each, the output
+ *                  feature is head * head_dim + d.
+ *   w_o [D, D]; w_gate_up [2F, D] with the gate rows first; w_down [D, F].
+ *   norm1_g, norm2_g [D]; q_g, k_g [head_dim];
+ *   ada [n_mod, 6, D]: the block's modulation table, chunks ordered shift_msa, scale_msa,
+ *                      gate_msa, shift_mlp, scale_mlp, gate_mlp. */
+typedef struct {
+  const uint16_t* w_qkv;
+  const uint16_t* w_o;
+  const uint16_t* w_gate_up;
+  const uint16_t* w_down;
+  const float* norm1_g;
+  const float* norm2_g;
+  const float* q_g;
+  const float* k_g;
+  const float* ada;
+} dit_block_weights;
+
+/* Velocity-reuse cache policy ([P1] section 3, MiniMaxH3DiTCacheConfig). mode DIT_CACHE_OFF
+ * or DIT_CACHE_VELOCITY ("conservative" is an alias resolved by the caller). Reuse happens
+ * only for progress i/N in [start_ratio, end_ratio), with a forced refresh every
+ * refresh_interval steps and at most max_consecutive_reuse reuses in a row. threshold must
+ * be NaN (the pages define only threshold=None). */
+typedef struct {
+  int32_t mode;
+  double start_ratio, end_ratio;
+  int32_t refresh_interval, max_consecutive_reuse;
+  double threshold;
+} dit_cache_policy;
+
+/* Work accounting of one denoise_loop call ([P2] "Purpose": only executed useful
+ * matrix/attention work counts). useful_flops = dit_calls * n_blocks *
+ * (8 V D^2 + 6 V D F + 4 V^2 D) with V = n_valid. step_hit: host uint8 [n_intervals] or NULL;
+ * when set it receives 1 for every reused interval. */
+typedef struct {
+  int32_t dit_calls, cache_hits;
+  int64_t executed_blocks, skipped_blocks;
+  double useful_flops;
+  uint8_t* step_hit;
+} dit_loop_stats;
+
+/* Byte offsets of the intermediates inside a workspace, for inspection after a call. Each
+ * is a row-major tensor with seq_pad rows whose tail rows are 0 after a block call:
+ *   h [L, D] bf16 (norm1 output), qkv [L, 3D] bf16 (q and k after Q/K norm and RoPE),
+ *   attn_out [L, D] bf16, x1 [L, D] fp32 (mid-block residual, kept fp32), h2 [L, D] bf16,
+ *   act [L, ffn_ld] bf16 (SwiGLU output, row stride ffn_ld; columns >= ffn undefined),
+ *   then the loop buffers (present when n_blocks >= 1): x_bf16, ping, pong, velocity,
+ *   each [L, D] bf16. */
+typedef struct {
+  size_t h, qkv, attn_out, x1, h2, act, x_bf16, ping, pong, velocity, total;
+  int64_t ffn_ld;
+} dit_workspace_map;
+
+/* Last error message of the calling thread ("" if none). Never NULL. */
+const char* dit_last_error(void);
+
+/* Library version string. */
+const char* dit_version(void);
+
+/* Hit/refresh schedule of a denoise loop ([P1] section 3): step_hit host uint8
+ * [n_intervals] receives 1 for each interval that reuses the previous velocity. Pure host
+ * work. Returns DIT_ERR_INVALID for a null pointer, n_intervals < 0, ratios outside [0, 1],
+ * start > end, refresh_interval < 1 or max_consecutive_reuse < 0; DIT_ERR_UNSUPPORTED for a
+ * non-NaN threshold or an unknown mode. */
+int dit_cache_schedule(const dit_cache_policy* policy, int32_t n_intervals, uint8_t* step_hit);
+
+/* Workspace needed by dit_block_forward (n_blocks = 0) or denoise_loop (n_blocks >= 1), and
+ * the offsets of its parts. Returns the size in bytes, or 0 with dit_last_error() set if the
+ * dims/layout are invalid or unsupported. map may be NULL. */
+size_t dit_workspace_size(const dit_dims* dims, const dit_layout* layout, int32_t n_blocks,
+                          dit_workspace_map* map);
+
+/* One joint audio-video DiT block ([P1] section 2; [P3] "Changes Made"):
+ *   E = ada + temb; h = RMSNorm(x) g1 (1 + E[m,1]) + E[m,0];
+ *   q,k,v = h Wqkv^T; q,k <- RoPE_neox(RMSNorm_head(q,k) g_{q,k});
+ *   o = softmax(q k^T / sqrt(head_dim)) v over the valid rows only;
+ *   x1 = x + E[m,2] (o Wo^T); h2 = RMSNorm(x1) g2 (1 + E[m,4]) + E[m,3];
+ *   x_out = x1 + E[m,5] ((silu(h2 Wg^T) * (h2 Wu^T)) Wd^T); tail rows of x_out are 0.
+ * temb: dev fp32 [n_mod, 6, D] timestep embedding. x_in, x_out: dev bf16 [seq_pad, D]; they
+ * may not alias each other or the workspace. attn_mode: DIT_ATTN_VALID_ONLY (work bounded by
+ * n_valid) or DIT_ATTN_FIXED_VALID (the whole padded length with a key mask); both give
+ * bitwise-identical outputs ([P1] section 5: the lossless modes are bit-exact).
+ * ws: dev workspace of at least dit_workspace_size(dims, layout, 0, NULL) bytes, 256-byte
+ * aligned; its contents on entry do not matter. stream: hipStream_t. */
+int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
+                      const dit_block_weights* weights, const float* temb,
+                      const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Flow-matching Euler update of the fp32 latent ([P3] "Changes Made": optimized scheduler
+ * updates with independent modality schedules): for valid rows of modality m,
+ * x += dt_m * v; x_bf16 = bf16(x) (the next DiT input). Tail rows of x and x_bf16 are set
+ * to 0. x: dev fp32 [seq_pad, hidden] in/out; v: dev bf16 [seq_pad, hidden]; x_bf16: dev
+ * bf16 [seq_pad, hidden], or NULL to skip the copy. hidden must be a multiple of 8. */
+int step_update(float* x, const uint16_t* v, uint16_t* x_bf16, const dit_layout* layout,
+                int32_t hidden, float dt_video, float dt_audio, void* stream);
+
+/* Cached denoise loop ([P1] sections 1 and 3): for each interval i the schedule of
+ * dit_cache_schedule decides refresh or reuse; on a refresh the n_blocks-block stack runs on
+ * bf16(x_i) with temb_steps[i] and its output is retained as the velocity (both modalities);
+ * on a reuse the retained velocity is used and no block runs; then
+ * x_{i+1} = x_i + (sigma_m[i+1] - sigma_m[i]) v per row modality.
+ *   blocks: host array [n_blocks] of dev weights; sigmas_video, sigmas_audio: host fp32
+ *   [n_intervals + 1]; temb_steps: dev fp32 [n_intervals, n_mod, 6, D];
+ *   x_latent: dev fp32 [seq_pad, D] in/out (tail rows are zero on return);
+ *   stats: host, filled from the schedule (may be NULL).
+ * Enqueues every step without a device-to-host synchronization. The per-request cache state
+ * (retained velocity, reuse counter) lives only in the workspace and in this call, and is
+ * gone when it returns, on success or error ([P2] "Purpose"). */
+int denoise_loop(const dit_dims* dims, const dit_layout* layout,
+                 const dit_block_weights* blocks, int32_t n_blocks, int32_t n_intervals,
+                 const float* sigmas_video, const float* sigmas_audio,
+                 const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
+                 int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Batched valid-only / fixed-valid attention ([P1] section 2). For request b, head h and
+ * query row i < valid_lens[b]: o = softmax_j(q_i . k_j / sqrt(head_dim)) v_j over
+ * j < valid_lens[b]; rows i >= valid_lens[b] of o are 0. q, k, v, o: dev bf16; element
+ * (b, i, h, d) is at ptr[b * batch_stride + i * row_stride + h * head_dim + d] (strides in
+ * elements, row_stride a multiple of 8; q, k, v share strides, o has its own). For the
+ * block's qkv buffer, q = qkv, k = qkv + D, v = qkv + 2D with row_stride 3D.
+ * valid_lens: host int32 [batch], each in [0, seq_pad]; batch <= 64; head_dim 64 or 128. */
+int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          uint16_t* o, int32_t batch, int32_t seq_pad, int32_t heads,
+                          int32_t head_dim, int64_t batch_stride, int64_t row_stride,
+                          int64_t o_batch_stride, int64_t o_row_stride,
+                          const int32_t* valid_lens, int32_t attn_mode, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AVDIT_H */

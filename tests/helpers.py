@@ -1,0 +1,75 @@
+"""Shared test utilities: tolerance checks and adapters from the seeded workloads to the oracle."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import oracle as O
+from audio_video_diffusion_dit_amd.inputs import Workload, bf16_to_f32
+
+# Floating-point parity bar for bf16 outputs: per-tensor max |err| <= 2e-2 * RMS(reference)
+# and cosine similarity >= 0.9995, over the valid rows.
+REL_MAX_ERR = 2e-2
+MIN_COSINE = 0.9995
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def close_stats(got, ref):
+    got = np.asarray(got, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    rms = float(math.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    den = float(np.linalg.norm(got) * np.linalg.norm(ref))
+    cos = float(np.dot(got, ref) / den) if den > 0 else (1.0 if err == 0 else 0.0)
+    return err, rms, cos
+
+
+def assert_close(got, ref, name: str, rel=REL_MAX_ERR, min_cos=MIN_COSINE):
+    err, rms, cos = close_stats(got, ref)
+    say(f"  {name}: max|err| {err:.3e}  RMS(ref) {rms:.3e}  ratio {err / max(rms, 1e-30):.2e}  cos {cos:.7f}")
+    assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
+    assert err <= rel * rms, f"{name}: max|err| {err:.3e} > {rel} * RMS {rms:.3e}"
+    assert cos >= min_cos, f"{name}: cosine {cos:.7f} < {min_cos}"
+    return err / max(rms, 1e-30), cos
+
+
+# Per-kernel bar for an intermediate stored in bf16 and fed the GPU's own input: a bf16 store
+# rounds by at most 2^-8 of the value's magnitude (8 significant bits); a kernel output carries
+# at most two such roundings (its bf16 input and its own output) plus fp32 arithmetic, so
+# max |err| <= 2^-6 * max |ref| leaves a factor-two margin, and the cosine must be >= 0.9999.
+KERNEL_REL_MAX = 2.0 ** -6
+KERNEL_MIN_COSINE = 0.9999
+
+
+def assert_kernel_close(got, ref, name: str):
+    ref = np.asarray(ref, dtype=np.float64)
+    amax = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err, rms, cos = close_stats(got, ref)
+    say(f"  {name}: max|err| {err:.3e}  max|ref| {amax:.3e}  ratio {err / max(amax, 1e-30):.2e}  "
+        f"err/RMS {err / max(rms, 1e-30):.2e}  cos {cos:.7f}")
+    assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
+    assert err <= KERNEL_REL_MAX * amax, f"{name}: max|err| {err:.3e} > 2^-6 * max|ref| {amax:.3e}"
+    assert cos >= KERNEL_MIN_COSINE, f"{name}: cosine {cos:.7f} < {KERNEL_MIN_COSINE}"
+
+
+def oracle_dims(wl: Workload) -> O.Dims:
+    return O.Dims(wl.hidden, wl.heads, wl.head_dim, wl.ffn, wl.norm_eps, wl.qk_eps, wl.rope_base)
+
+
+def oracle_layout(wl: Workload) -> O.Layout:
+    return O.Layout(wl.n_video, wl.n_audio, wl.seq_pad)
+
+
+def oracle_block(bp) -> dict:
+    return {k: np.asarray(v, dtype=np.float64) for k, v in bp.as_float().items()}
+
+
+def x_values(bits) -> np.ndarray:
+    return bf16_to_f32(bits).astype(np.float64)

@@ -1,0 +1,178 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every declared entry point, its
+host-side cache schedule equals the oracle's, and invalid arguments are rejected before any
+device work (none of these calls touches a GPU)."""
+
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def N():
+    from audio_video_diffusion_dit_amd import _native
+    return _native
+
+
+def test_library_exports_every_declared_symbol(N):
+    with open(os.path.join(ROOT, "include", "avdit.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", header, re.M))
+    declared -= {"if", "return"}
+    assert {"dit_block_forward", "denoise_loop", "step_update"} <= declared
+    for name in declared:
+        assert hasattr(N.lib, name), f"{name} is declared but not exported"
+    assert set(N.EXPORTED) == declared
+    assert N.lib.dit_version().decode().startswith("avdit")
+
+
+RATIOS = [(0.2, 0.8), (0.0, 1.0), (0.0, 0.0), (0.5, 0.5), (0.1, 0.9), (0.25, 0.75), (0.3, 0.31),
+          (0.0, 0.5), (0.5, 1.0), (1.0, 1.0)]
+
+
+@pytest.mark.parametrize("r,c", [(2, 1), (1, 1), (3, 2), (3, 1), (4, 9), (2, 0), (5, 3)])
+def test_schedule_matches_oracle(N, r, c):
+    for s, e in RATIOS:
+        for n in range(0, 201):
+            pol = O.CachePolicy("velocity", s, e, r, c)
+            want = O.cache_schedule(pol, n)
+            got = N.dit_cache_schedule(N.make_policy("conservative", s, e, r, c), n)
+            assert got == want, (s, e, r, c, n)
+    off = N.dit_cache_schedule(N.make_policy("off"), 49)
+    assert off == [False] * 49
+
+
+def test_schedule_counts_printed_on_pages(N):
+    hits = N.dit_cache_schedule(N.make_policy("conservative"), 49)
+    assert (49 - sum(hits), sum(hits)) == (34, 15)
+    assert N.dit_cache_schedule(N.make_policy("velocity", quality="high"), 49) == [False] * 49
+
+
+def test_policy_validation(N):
+    bad = [dict(start_ratio=-0.1), dict(end_ratio=1.5), dict(start_ratio=0.9, end_ratio=0.1),
+           dict(refresh_interval=0), dict(max_consecutive_reuse=-1)]
+    for kw in bad:
+        with pytest.raises(N.AvditError) as ei:
+            N.dit_cache_schedule(N.make_policy("conservative", **kw), 49)
+        assert ei.value.code == N.DIT_ERR_INVALID
+        assert N.last_error()
+    with pytest.raises(N.AvditError) as ei:
+        N.dit_cache_schedule(N.make_policy("conservative", threshold=0.05), 49)
+    assert ei.value.code == N.DIT_ERR_UNSUPPORTED
+    p = N.make_policy("conservative")
+    p.mode = 7
+    with pytest.raises(N.AvditError) as ei:
+        N.dit_cache_schedule(p, 49)
+    assert ei.value.code == N.DIT_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        N.resolve_mode("bogus")
+    # a valid call after failures clears the error and is unaffected by them
+    assert sum(N.dit_cache_schedule(N.make_policy("conservative"), 49)) == 15
+    assert N.last_error() == ""
+
+
+def test_dims_and_layout_validation(N):
+    lay = N.make_layout(512, 96, 640)
+    cases = [
+        (N.make_dims(256, 4, 60, 683), N.DIT_ERR_UNSUPPORTED),   # head_dim
+        (N.make_dims(256, 3, 64, 683), N.DIT_ERR_INVALID),       # D != H * Dh
+        (N.make_dims(256, 4, 64, 0), N.DIT_ERR_INVALID),         # ffn
+        (N.make_dims(256, 4, 64, 683, n_mod=3), N.DIT_ERR_UNSUPPORTED),
+        (N.make_dims(256, 4, 64, 683, norm_eps=float("nan")), N.DIT_ERR_INVALID),
+        (N.make_dims(256, 4, 64, 683, rope_base=0.0), N.DIT_ERR_INVALID),
+    ]
+    for dims, code in cases:
+        with pytest.raises(N.AvditError):
+            N.dit_workspace_size(dims, lay)
+        assert N.last_error()
+    d = N.make_dims(256, 4, 64, 683)
+    for bad_lay in (N.make_layout(512, 96, 600), N.make_layout(-1, 96, 640)):
+        with pytest.raises(N.AvditError):
+            N.dit_workspace_size(d, bad_lay)
+
+
+def test_workspace_map(N):
+    d = N.make_dims(3072, 24, 128, 8192)
+    lay = N.make_layout(12096, 1344, 13568)
+    n0, m0 = N.dit_workspace_size(d, lay, 0)
+    n1, m1 = N.dit_workspace_size(d, lay, 1)
+    L, D = 13568, 3072
+    assert m0.ffn_ld == 8192
+    offs = [m0.h, m0.qkv, m0.attn_out, m0.x1, m0.h2, m0.act]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert m0.qkv - m0.h >= L * D * 2 and m0.attn_out - m0.qkv >= L * 3 * D * 2
+    assert n0 >= m0.act + L * 8192 * 2
+    assert n1 == n0 + 4 * (L * D * 2)
+    _, m = N.dit_workspace_size(N.make_dims(256, 4, 64, 683), N.make_layout(512, 96, 640), 0)
+    assert m.ffn_ld == 688
+
+
+def test_entry_points_reject_invalid_arguments_without_device_work(N):
+    d = N.make_dims(256, 4, 64, 683)
+    lay = N.make_layout(512, 96, 640)
+    w = N.DitBlockWeights(*([256] * 9))   # fake non-null addresses: never dereferenced
+    null_w = N.DitBlockWeights()
+    ws_need, _ = N.dit_workspace_size(d, lay, 0)
+    big = 1 << 40
+    # null weights
+    code = N.lib.dit_block_forward(d, lay, null_w, 256, 256, 512, 0, big, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    # bad attention mode
+    code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 30, 5, big, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    # workspace too small
+    code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 30, 0, big, ws_need - 1, None)
+    assert code == N.DIT_ERR_WORKSPACE
+    # misaligned workspace
+    code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 30, 0, big + 8, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    # aliasing input and output
+    code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 20, 0, big, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    # step_update: hidden not a multiple of 8, non-finite step
+    assert N.lib.step_update(1 << 20, 1 << 21, None, lay, 100, -0.1, -0.1, None) == N.DIT_ERR_INVALID
+    assert N.lib.step_update(1 << 20, 1 << 21, None, lay, 256, math.inf, -0.1, None) == N.DIT_ERR_INVALID
+    # attention: head_dim, batch, valid length, strides
+    vl = (N.c_int32 * 2)(10, 700)
+    assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 2, 640, 4, 64, 640 * 256,
+                                       256, 640 * 256, 256, vl, 0, None) == N.DIT_ERR_INVALID
+    vl = (N.c_int32 * 1)(10)
+    assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1, 640, 4, 96, 0,
+                                       384, 0, 384, vl, 0, None) == N.DIT_ERR_UNSUPPORTED
+    assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 0, 640, 4, 64, 0,
+                                       256, 0, 256, vl, 0, None) == N.DIT_ERR_INVALID
+    assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1, 640, 4, 64, 0,
+                                       200, 0, 256, vl, 0, None) == N.DIT_ERR_INVALID
+
+
+def test_denoise_loop_rejects_invalid_arguments(N):
+    d = N.make_dims(256, 4, 64, 683)
+    lay = N.make_layout(512, 96, 640)
+    w = (N.DitBlockWeights * 1)(N.DitBlockWeights(*([256] * 9)))
+    need, _ = N.dit_workspace_size(d, lay, 1)
+    sig = (N.c_float * 50)(*np.linspace(1, 0, 50).astype(np.float32))
+    stats = N.DitLoopStats()
+    pol = N.make_policy("conservative")
+    big = 1 << 40
+    args = lambda **kw: dict(dict(dims=d, lay=lay, blocks=w, nb=1, n=49, sv=sig, sa=sig, temb=256,
+                                  pol=pol, x=1 << 20, mode=0, stats=stats, ws=big, wsb=need), **kw)
+
+    def call(a):
+        return N.lib.denoise_loop(a["dims"], a["lay"], a["blocks"], a["nb"], a["n"], a["sv"], a["sa"],
+                                  a["temb"], a["pol"], a["x"], a["mode"], a["stats"], a["ws"],
+                                  a["wsb"], None)
+
+    assert call(args(nb=0)) == N.DIT_ERR_INVALID
+    assert call(args(n=-1)) == N.DIT_ERR_INVALID
+    assert call(args(wsb=need - 256)) == N.DIT_ERR_WORKSPACE
+    bad = N.make_policy("conservative", threshold=0.1)
+    assert call(args(pol=bad)) == N.DIT_ERR_UNSUPPORTED
+    nan_sig = (N.c_float * 50)(*([float("nan")] * 50))
+    assert call(args(sv=nan_sig)) == N.DIT_ERR_INVALID
+    assert call(args(blocks=(N.DitBlockWeights * 1)(N.DitBlockWeights()))) == N.DIT_ERR_INVALID
