@@ -4,22 +4,31 @@
 //
 // Design for gfx950:
 //  * A workgroup (4 wave64s) owns 128 queries of one (request, head); each wave owns 32 queries
-//    and keeps its Q fragments in registers for the whole key sweep.
+//    and keeps its Q fragments in registers for the whole key sweep. Two workgroups share a CU,
+//    so one wave's softmax overlaps the other wave's matrix work on each SIMD.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (K tile from
 //    LDS as the A operand, Q as the B operand): each lane then holds 32 of the 64 scores of
-//    one query per key tile, so the running max and sum need only one cross-lane exchange
-//    (lanes l and l^32).
+//    one query per key tile, so the running max needs one cross-lane exchange (lanes l, l^32).
 //  * O^T = V^T P^T reuses the score registers directly as the B operand: the k index of that
-//    MFMA is mapped onto keys in the order the score layout already has, and V is written to
-//    LDS transposed and in that same key order, so both operands are single 16-byte reads.
-//  * K/V tiles of 64 keys are double buffered in LDS with one barrier per tile; the next
-//    tile's global loads are in flight during the current tile's math.
+//    MFMA is mapped onto keys in the order the score layout already has. V stays row-major in
+//    LDS, like K, and its A-operand fragments are assembled by the LDS transpose read
+//    (ds_read_b64_tr_b16): within 16 lanes it turns four 4-element row pieces into four
+//    4-key columns, so V needs no transposition work on the way in.
+//  * K/V tiles of 64 keys go straight from memory into LDS (buffer loads with the LDS
+//    destination, no staging registers); the resource range ends at the request's valid
+//    length, so keys past it read as zero. Tiles are double buffered with one barrier per
+//    tile, and the next tile's loads are in flight during the current tile's math. The key
+//    loop is unrolled by two so that both LDS buffers are addressed with immediate offsets.
+//  * Only the last partial tile (and, in fixed-valid mode, the tiles past the valid length)
+//    run the masking code, and the accumulator rescale runs only on tiles where some row's
+//    maximum grew.
 //  * Valid-only mode bounds the key sweep by the request's valid length and query tiles that
 //    lie wholly in the tail only write zeros. Fixed-valid mode sweeps the whole padded
-//    length with a key mask. Keys at or past the valid length are loaded as zero and scored
-//    -inf, so a fully masked tile leaves the running max, the sum and the accumulator
-//    unchanged bit for bit: the two modes give identical outputs.
+//    length with a key mask. A fully masked tile leaves the running max, the sum and the
+//    accumulator unchanged bit for bit, so the two modes give identical outputs.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -28,32 +37,64 @@ namespace avdit {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kQB = 128;  // queries per workgroup
-constexpr int kKB = 64;   // keys per tile
+constexpr int kQB = 128;                    // queries per workgroup
+constexpr int kKB = 64;                     // keys per tile
+constexpr int32_t kAttnRsrcWord3 = 0x00020000;
 
-// XOR swizzle of the 16-byte chunk index of a V^T row (row = head-dim index d).
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+// 16-byte-chunk XOR swizzle of a K row: 16 consecutive rows read at one logical chunk hit
+// distinct banks (rows are 256 bytes at head_dim 128, 128 bytes at 64).
+template <int DH>
+__device__ __forceinline__ int kswz(int row) {
+  return DH == 128 ? (row & 15) : ((row ^ (row >> 3)) & 7);
+}
+// Swizzle of a V row for the transpose reads: the 4 key rows x 32 bytes that one pair of
+// 16-lane groups reads land on 16 distinct 16-byte bank groups.
+template <int DH>
+__device__ __forceinline__ int vswz(int key) {
+  return DH == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+}
 
-// Position of key group g4 (keys 4 g4 .. 4 g4 + 3 of a 64-key tile) inside a V^T row: within
-// each 16 keys the order is [0-3, 8-11, 4-7, 12-15], the order in which one score lane-half
-// holds keys for the P V product.
-__device__ __forceinline__ int vt_pos(int g4) {
-  const int q4 = g4 & 3;
-  return (g4 >> 2) * 16 + (((q4 & 1) << 1) | (q4 >> 1)) * 4;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           kAttnRsrcWord3);
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource as four SGPR words: base, range in bytes, 32-bit-element format.
+__device__ __forceinline__ i32x4 attn_rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t ad = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int32_t)(uint32_t)ad, (int32_t)(uint32_t)(ad >> 32), (int32_t)bytes, kAttnRsrcWord3};
+}
+
+// One 16-byte-per-lane buffer load written straight into LDS: lane l's chunk lands at LDS byte
+// address lds_base + 16 l (lds_base uniform across the wave). Offsets past the resource range
+// read as zero. Issued as inline assembly so that the compiler does not serialise later LDS
+// reads behind it; completion is awaited explicitly with s_waitcnt vmcnt before the barrier
+// that publishes the tile.
+__device__ __forceinline__ void dma_b128(uint32_t lds_base, uint32_t voffset, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
 }
 
 template <int DH>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
-  constexpr int NC = DH / 8;        // 16-byte chunks per q/k row
-  constexpr int QS = DH / 16;       // k-steps of the score MFMA
-  constexpr int DT = DH / 32;       // 32-row tiles of O^T
-  constexpr int KCH = kKB * NC;     // chunks in a K tile
-  constexpr int KPT = KCH / 256;    // K chunks staged per thread
-  constexpr int VIT = (16 * NC + 255) / 256;  // (key group, d chunk) items per thread
+  constexpr int NC = DH / 8;          // 16-byte chunks per K/V row
+  constexpr int QS = DH / 16;         // k-steps of the score MFMA
+  constexpr int DT = DH / 32;         // 32-row tiles of O^T
+  constexpr int TILE = kKB * NC;      // 16-byte chunks per K (or V) tile
+  constexpr int LPT = TILE / 256;     // chunks each thread stages per operand per tile
+  constexpr int VOFF = TILE * 16;     // byte offset of the V tile inside a buffer
+  constexpr int BUFB = 2 * TILE * 16; // bytes per buffer
 
-  __shared__ u32x4 ks[2][KCH];
-  __shared__ u32x4 vts[2][DH * 8];
+  __shared__ u32x4 smem[2 * 2 * TILE];  // [buffer][K tile | V tile]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,65 +131,66 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     qf[s] = __builtin_bit_cast(bf16x8, w);
   }
 
-  const int key_end = a.fixed_valid ? L : V;
-  const int nkt = (key_end + kKB - 1) / kKB;
+  // ---- global -> LDS staging: wave w's i-th load fills 16-byte slots (4 i + w) * 64 + lane of
+  // a tile, i.e. row p / NC and physical chunk p % NC of slot p; the lane fetches the logical
+  // chunk that the swizzle places there. Keys >= V read as zero (resource range). ----
+  const uint32_t span = (uint32_t)((int64_t)V * a.row_stride * 2);
+  const i32x4 rs_k = attn_rsrc_words(K, span);
+  const i32x4 rs_v = attn_rsrc_words(Vp, span);
+  const uint32_t tile_bytes = (uint32_t)(kKB * a.row_stride * 2);
+  // At head_dim 128 successive loads of a wave are 16 rows apart and both swizzles have period
+  // 16 in the row, so one offset per operand plus a uniform stride covers them.
+  constexpr int GK = (DH == 128) ? 1 : LPT;
+  uint32_t goff_k[GK], goff_v[GK];
+#pragma unroll
+  for (int i = 0; i < GK; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    const int row = p / NC, pc = p % NC;
+    goff_k[i] = (uint32_t)(row * a.row_stride * 2 + (pc ^ kswz<DH>(row)) * 16);
+    goff_v[i] = (uint32_t)(row * a.row_stride * 2 + (pc ^ vswz<DH>(row)) * 16);
+  }
+  const uint32_t gstep = (uint32_t)(4 * 64 / NC * a.row_stride * 2);  // rows between loads
+  lds_char* lds = (lds_char*)(smem);  // __shared__ array viewed in the LDS address space
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)lds + wave * 1024);
+  auto load_tile = [&](int kt, int buf) {
+    const uint32_t g = (uint32_t)kt * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t ok = (DH == 128) ? goff_k[0] + i * gstep : goff_k[i % GK];
+      const uint32_t ov = (DH == 128) ? goff_v[0] + i * gstep : goff_v[i % GK];
+      dma_b128(lds0 + buf * BUFB + i * 4096, g + ok, rs_k);
+      dma_b128(lds0 + buf * BUFB + VOFF + i * 4096, g + ov, rs_v);
+    }
+  };
 
-  u32x4 kst[KPT];
-  u32x4 vst[VIT][4];
-  auto load_tile = [&](int kt) {
-    const int kv0 = kt * kKB;
+  // ---- per-lane LDS read addresses (byte offsets inside buffer 0) ----
+  // K fragment of score k-step s, key half h2: row 32 h2 + l32, logical chunk 2 s + hh. At
+  // head_dim 128 the swizzle ignores h2, which then only adds 32 rows.
+  constexpr int KH = (DH == 128) ? 1 : 2;
+  int kaddr[KH][QS];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int q = tid + 256 * i;
-      const int key = kv0 + q / NC;
-      kst[i] = (key < V) ? *reinterpret_cast<const u32x4*>(K + (int64_t)key * a.row_stride + (q % NC) * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
+  for (int h2 = 0; h2 < KH; ++h2)
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      const int row = h2 * 32 + l32;
+      kaddr[h2][s] = (row * NC + ((2 * s + hh) ^ kswz<DH>(row))) * 16;
     }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int idx = tid + 256 * it;
-      const int g4 = idx / NC, dc = idx % NC;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + 4 * g4 + r;
-        vst[it][r] = (idx < 16 * NC && key < V)
-                         ? *reinterpret_cast<const u32x4*>(Vp + (int64_t)key * a.row_stride + dc * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  auto kaddr_of = [&](int h2, int s) {
+    return (DH == 128) ? kaddr[0][s] + h2 * 32 * NC * 16 : kaddr[h2 % KH][s];
   };
-  auto store_tile = [&](int buf) {
+  // V^T fragment of d-tile dt: lane group g = lane / 16 supplies rows key0 + (lane & 15) / 4 and
+  // columns 32 dt + 16 (g & 1) + 4 (lane & 3); key0 = 16 ps + 8 r + 4 (g >> 1) is added per read.
+  int vaddr[DT];
+  {
+    const int g = lane >> 4, s16 = lane & 15;
+    const int key = 4 * (g >> 1) + (s16 >> 2);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int q = tid + 256 * i;
-      const int row = q / NC, c = q % NC;
-      ks[buf][row * NC + (c ^ (row & (NC - 1)))] = kst[i];
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+      vaddr[dt] = VOFF + key * NC * 16 + (((d >> 3) ^ vswz<DH>(key)) * 16) + (d & 7) * 2;
     }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int idx = tid + 256 * it;
-      if (idx < 16 * NC) {
-        const int g4 = idx / NC, dc = idx % NC;
-        const int p = vt_pos(g4);
-        u32x2* vt2 = reinterpret_cast<u32x2*>(vts[buf]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // element e of the 8-wide d chunk, for the 4 keys of the group
-          const int wsel = e >> 1;
-          const bool hi = e & 1;
-          uint32_t k4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t w = vst[it][r][wsel];
-            k4[r] = hi ? (w >> 16) : (w & 0xFFFFu);
-          }
-          const int d = dc * 8 + e;
-          const int chunk = (p >> 3) ^ vt_swz(d);
-          vt2[d * 16 + chunk * 2 + ((p & 7) >> 2)] = u32x2{k4[0] | (k4[1] << 16), k4[2] | (k4[3] << 16)};
-        }
-      }
-    }
-  };
+  }
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -159,13 +201,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   float l_run = 0.0f;
   const float c = a.scale_log2;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const int kv0 = kt * kKB;
-    if (kt + 1 < nkt) load_tile(kt + 1);
+  const int key_end = a.fixed_valid ? L : V;
+  const int nkt = (key_end + kKB - 1) / kKB;
+  const int n_full = V / kKB;  // tiles whose 64 keys are all valid
+
+  auto tile = [&](auto masked_c, auto buf_c, int kt) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int BUF = decltype(buf_c)::value;
+    const bool more = kt + 1 < nkt;
+    if (more) load_tile(kt + 1, BUF ^ 1);
 
     // ---- S^T = K Q^T for 64 keys x 32 queries ----
     f32x16 sacc[2];
@@ -175,14 +219,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
-        const int row = h2 * 32 + l32;
-        const int ch = (2 * s + hh) ^ (row & (NC - 1));
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, ks[cur][row * NC + ch]);
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + BUF * BUFB + kaddr_of(h2, s)));
         sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[h2], 0, 0, 0);
       }
     }
-    // element (j, i) of sacc[h2] is key kv0 + 32 h2 + 8 j + 4 hh + i
-    if (kv0 + kKB > V) {
+    // element (j, i) of sacc[h2] is key kt * 64 + 32 h2 + 8 j + 4 hh + i
+    if (MASKED) {
+      const int kv0 = kt * kKB;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -192,18 +236,27 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         }
     }
 
-    // ---- online softmax (base 2, scale folded into c) ----
+    // ---- online softmax in base 2 with the scale folded into c ----
     float mx = sacc[0][0];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // The running max is exact (the largest probability of a row is exactly 1). The
+    // accumulator rescale is skipped when no lane's max grew: alpha would be exactly 1.
     const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-    m_run = m_new;
-    const float mc = m_use * c;
+    const bool grow = m_new > m_run;  // false for a fully masked tile (mx = -inf)
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c;
     float psum = 0.0f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -213,11 +266,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         sacc[h2][e] = p;
         psum += p;
       }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T, 4 k-steps of 16 keys ----
 #pragma unroll
@@ -231,15 +280,32 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{p0, p1, p2, p3});
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const int d = t * 32 + l32;
-        const int ch = (2 * ps + hh) ^ vt_swz(d);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vts[cur][d * 8 + ch]);
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
+        lds_char* base = lds + BUF * BUFB + vaddr[t] + (16 * ps) * NC * 16;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(base));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(base + 8 * NC * 16));
+        const s16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf,
+                                                          oacc[t], 0, 0, 0);
       }
     }
 
-    if (kt + 1 < nkt) store_tile(cur ^ 1);
+    if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= n_full; kt += 2) {
+    tile(std::false_type{}, std::integral_constant<int, 0>{}, kt);
+    tile(std::false_type{}, std::integral_constant<int, 1>{}, kt + 1);
+  }
+  for (; kt < nkt; ++kt) {
+    if (kt & 1)
+      tile(std::true_type{}, std::integral_constant<int, 1>{}, kt);
+    else
+      tile(std::true_type{}, std::integral_constant<int, 0>{}, kt);
   }
 
   // ---- normalise and store: element (j, i) of oacc[t] is d = 32 t + 8 j + 4 hh + i ----
@@ -267,6 +333,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if ((a.row_stride & 7) != 0 || (a.o_row_stride & 7) != 0 || (a.batch_stride & 7) != 0 ||
       (a.o_batch_stride & 7) != 0)
     return hipErrorInvalidValue;
+  // buffer offsets are 32-bit: one request's rows must span less than 2 GiB
+  if ((int64_t)a.seq_pad * a.row_stride * 2 >= (int64_t)0x80000000) return hipErrorInvalidValue;
   if (a.seq_pad == 0) return hipSuccess;
   const dim3 grid((a.seq_pad + kQB - 1) / kQB, a.heads, a.batch);
   if (a.head_dim == 128) {

@@ -1,24 +1,29 @@
 // bf16 MFMA GEMM for the block's projections: C[m][n] = sum_k A[m][k] * W[n][k], both operands
 // contiguous along k (activations [tokens, K], weights [out, in]), fp32 accumulation, with the
-// epilogue fused: plain store (QKV), gated residual (out-projection into the fp32 mid-block residual, down-projection from it), or
-// SwiGLU over interleaved gate/up weight rows (gate/up projection, TeleFuser PR #23, "Changes
-// Made": fused SwiGLU).
+// epilogue fused: plain store (QKV), gated residual (out-projection into the fp32 mid-block
+// residual, down-projection from it), or SwiGLU over interleaved gate/up weight rows (gate/up
+// projection; TeleFuser PR #23, "Changes Made": fused SwiGLU).
 //
 // Design for gfx950:
-//  * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (BN/2 features) x (BM/2 tokens)
-//    accumulator block made of 32x32 tiles of v_mfma_f32_32x32x16_bf16. The weight tile is the
-//    MFMA A operand and the token tile the B operand, so every lane ends up holding 4
-//    consecutive output features of one token: epilogue loads/stores are 8-byte vectors.
-//  * k-tiles of 64 staged through LDS, double buffered, one barrier per k-tile; the next tile's
-//    global loads are in flight while the current one is multiplied. LDS rows are 128 bytes with
-//    the 16-byte chunk index XOR-swizzled by (row & 7), which keeps both the 16-byte fragment
-//    reads (32 rows, same chunk) and the loader's writes free of bank conflicts.
+//  * WM x WN wave64s per workgroup; each wave owns a (BN/WN features) x (BM/WM tokens)
+//    accumulator block of 32x32 tiles of v_mfma_f32_32x32x16_bf16. The weight tile is the MFMA
+//    A operand and the token tile the B operand, so every lane ends up holding 4 consecutive
+//    output features of one token: epilogue loads/stores are 8- or 16-byte vectors.
+//  * k-tiles of 64 staged global -> registers -> LDS, double buffered, one barrier per k-tile.
+//    Global loads are raw buffer loads: rows past the valid range or past K read as zero from
+//    the hardware's range check, so the loop has no branches. The next tile's loads are issued
+//    at the top of the current tile and written to the other LDS buffer after the current
+//    tile's last MFMAs have been issued.
+//  * MFMA fragments are double buffered in registers: the fragments of k-substep s+1 are read
+//    from LDS while the MFMAs of substep s run, so LDS latency hides under matrix work.
+//  * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by (r ^ r >> 3) & 7,
+//    which keeps both the 16-byte fragment reads (32 rows, same chunk) and the loader's writes
+//    free of bank conflicts.
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
 //    receives a contiguous range of tiles, and tiles are ordered in groups of 8 token-tiles,
-//    so the workgroups resident on one XCD share both operand panels in that XCD's L2.
-//  * Rows at or beyond n_valid are never multiplied: their loads are predicated to zero and a
-//    tile that lies entirely in the tail only writes zeros (the zero-tail merge of TeleFuser
-//    PR #38, section 2).
+//    so the workgroups resident on one XCD share operand panels in that XCD's L2.
+//  * Rows at or beyond n_valid are never multiplied: their loads read zero and a tile that lies
+//    entirely in the tail only writes zeros (the zero-tail merge of TeleFuser PR #38, section 2).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,14 +32,19 @@ namespace avdit {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;  // k-tile; 8 chunks of 8 bf16 per LDS row
+constexpr int kBK = 64;                      // k-tile; 8 chunks of 8 bf16 per LDS row
+constexpr uint32_t kOob = 0x80000000u;       // buffer offset past every range: reads zero
+constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit elements
 
-template <bool ALIGNED>
-__device__ __forceinline__ u32x4 load_chunk(const uint16_t* __restrict__ base, int64_t ld,
-                                            int row, bool row_ok, int k, int K) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Element-wise load of 8 bf16 at (row, k) for operands whose rows are not 16-byte aligned.
+__device__ __forceinline__ u32x4 load_chunk_slow(const uint16_t* __restrict__ base, int64_t ld,
+                                                 int row, bool row_ok, int k, int K) {
   if (!row_ok || k >= K) return u32x4{0u, 0u, 0u, 0u};
   const uint16_t* p = base + (int64_t)row * ld + k;
-  if (ALIGNED) return *reinterpret_cast<const u32x4*>(p);
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -45,19 +55,28 @@ __device__ __forceinline__ u32x4 load_chunk(const uint16_t* __restrict__ base, i
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row. Sixteen consecutive rows
+// read at one logical chunk land on distinct banks whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per cycle: f is a permutation on every 8 aligned rows, and injective on the even
+// and on the odd rows of every 16.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-template <int BM, int BN, int EPI, bool ALIGNED>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int tiles_n) {
-  constexpr int TM = BM / 2;          // tokens per wave
-  constexpr int TN = BN / 2;          // weight rows per wave
+template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int NT = 64 * WM * WN;    // threads
+  constexpr int TM = BM / WM;         // tokens per wave
+  constexpr int TN = BN / WN;         // weight rows per wave
   constexpr int MT = TM / 32;         // 32-token sub-tiles per wave
   constexpr int FT = TN / 32;         // 32-row weight sub-tiles per wave
   constexpr int ROWS = BM + BN;       // LDS rows per stage (weights first)
-  constexpr int PT = ROWS * 8 / 256;  // 16-byte chunks each thread stages per k-tile
+  constexpr int PT = ROWS * 8 / NT;   // 16-byte chunks each thread stages per k-tile
+  constexpr int RPI = NT / 8;         // LDS rows covered by one staging step
   static_assert(EPI != EPI_SWIGLU || (FT % 2) == 0, "SwiGLU pairs gate/up sub-tiles");
+  static_assert(BN % RPI == 0 && BM % RPI == 0, "staging steps must not straddle operands");
 
   __shared__ u32x4 lds[2][ROWS * 8];
 
@@ -66,8 +85,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int ti
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int wave = tid >> 6;
-  const int wm = wave & 1;   // token half
-  const int wn = wave >> 1;  // feature half
+  const int wm = wave % WM;   // token slice
+  const int wn = wave / WM;   // feature slice
 
   // ---- tile selection: XCD-contiguous ranges, grouped token-tile order ----
   const int nt = tiles_m * tiles_n;
@@ -98,14 +117,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int ti
       for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.0f;
 
   if (m0 < n_valid) {
-    // ---- staging map: chunk q = tid + 256 i -> LDS row q / 8, chunk q % 8 ----
     const int ck = tid & 7;
+    const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A, (uint32_t)((int64_t)seq_pad * a.lda * 2));
+    // byte offset of each staged row (kOob when the row is masked)
+    uint32_t src_off[PT];
     int src_row[PT];
     bool src_ok[PT];
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      if (r < BN) {
+      const int r = (tid >> 3) + RPI * i;
+      if (i < BN / RPI) {
         int wrow, feat;
         if (EPI == EPI_SWIGLU) {
           const int blk = r >> 5;
@@ -117,10 +140,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int ti
         }
         src_row[i] = wrow;
         src_ok[i] = feat < a.N;
+        src_off[i] = src_ok[i] ? (uint32_t)((int64_t)wrow * a.ldw * 2) : kOob;
       } else {
         const int tok = m0 + (r - BN);
         src_row[i] = tok;
         src_ok[i] = tok < n_valid;
+        src_off[i] = src_ok[i] ? (uint32_t)((int64_t)tok * a.lda * 2) : kOob;
       }
     }
     const int nk = (a.K + kBK - 1) / kBK;
@@ -129,48 +154,62 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int ti
       const int k = kt * kBK + ck * 8;
 #pragma unroll
       for (int i = 0; i < PT; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        stage[i] = (r < BN) ? load_chunk<ALIGNED>(a.W, a.ldw, src_row[i], src_ok[i], k, a.K)
-                            : load_chunk<ALIGNED>(a.A, a.lda, src_row[i], src_ok[i], k, a.K);
+        // staging step i covers rows RPI*i .. RPI*i + RPI - 1: all weight rows or all token rows
+        const bool w_step = i < BN / RPI;
+        if (ALIGNED) {
+          const uint32_t off = (k < a.K) ? src_off[i] + (uint32_t)(k * 2) : kOob;
+          stage[i] = w_step ? __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0)
+                            : __builtin_amdgcn_raw_buffer_load_b128(rs_a, off, 0, 0);
+        } else {
+          stage[i] = w_step ? load_chunk_slow(a.W, a.ldw, src_row[i], src_ok[i], k, a.K)
+                            : load_chunk_slow(a.A, a.lda, src_row[i], src_ok[i], k, a.K);
+        }
       }
     };
     auto store_stage = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < PT; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        lds[buf][r * 8 + (ck ^ (r & 7))] = stage[i];
+        const int r = (tid >> 3) + RPI * i;
+        lds[buf][r * 8 + (ck ^ swz(r))] = stage[i];
+      }
+    };
+    bf16x8 af[2][FT], bf[2][MT];
+    auto read_frags = [&](int buf, int s, int slot) {
+      const int c = 2 * s + hh;
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const int r = wn * TN + f * 32 + l32;
+        af[slot][f] = __builtin_bit_cast(bf16x8, lds[buf][r * 8 + (c ^ swz(r))]);
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int r = BN + wm * TM + t * 32 + l32;
+        bf[slot][t] = __builtin_bit_cast(bf16x8, lds[buf][r * 8 + (c ^ swz(r))]);
       }
     };
 
     load_stage(0);
     store_stage(0);
     __syncthreads();
+    read_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) load_stage(kt + 1);
-      const u32x4* L = lds[cur];
+      const bool more = kt + 1 < nk;
+      if (more) load_stage(kt + 1);
 #pragma unroll
       for (int s = 0; s < kBK / 16; ++s) {
-        const int c = 2 * s + hh;
-        bf16x8 af[FT], bf[MT];
-#pragma unroll
-        for (int f = 0; f < FT; ++f) {
-          const int r = wn * TN + f * 32 + l32;
-          af[f] = __builtin_bit_cast(bf16x8, L[r * 8 + (c ^ (r & 7))]);
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int r = BN + wm * TM + t * 32 + l32;
-          bf[t] = __builtin_bit_cast(bf16x8, L[r * 8 + (c ^ (r & 7))]);
-        }
+        const int slot = s & 1;
+        if (s + 1 < kBK / 16) read_frags(cur, s + 1, slot ^ 1);
 #pragma unroll
         for (int f = 0; f < FT; ++f)
 #pragma unroll
           for (int t = 0; t < MT; ++t)
-            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f], bf[t], acc[f][t], 0, 0, 0);
+            acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][f], bf[slot][t],
+                                                                acc[f][t], 0, 0, 0);
       }
-      if (kt + 1 < nk) store_stage(cur ^ 1);
+      if (more) store_stage(cur ^ 1);
       __syncthreads();
+      if (more) read_frags(cur ^ 1, 0, 0);
     }
   }
 
@@ -237,25 +276,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a, int tiles_m, int ti
   }
 }
 
-template <int BM, int BN, int EPI, bool ALIGNED>
+template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
 static hipError_t gemm_instance(const GemmArgs& a, hipStream_t s) {
   const int out_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (a.rows.seq_pad + BM - 1) / BM;
   const int tiles_n = (a.N + out_per_tile - 1) / out_per_tile;
   const int nt = tiles_m * tiles_n;
   if (nt == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<BM, BN, EPI, ALIGNED>), dim3(nt), dim3(256), 0, s, a, tiles_m,
-                     tiles_n);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, ALIGNED>), dim3(nt), dim3(64 * WM * WN), 0, s,
+                     a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int BM, int BN, bool ALIGNED>
+template <int BM, int BN, int WM, int WN, bool ALIGNED>
 static hipError_t gemm_dispatch_epi(const GemmArgs& a, hipStream_t s) {
   switch (a.epilogue) {
-    case EPI_STORE: return gemm_instance<BM, BN, EPI_STORE, ALIGNED>(a, s);
-    case EPI_GATED_TO_F32: return gemm_instance<BM, BN, EPI_GATED_TO_F32, ALIGNED>(a, s);
-    case EPI_GATED_F32_IN: return gemm_instance<BM, BN, EPI_GATED_F32_IN, ALIGNED>(a, s);
-    case EPI_SWIGLU: return gemm_instance<BM, BN, EPI_SWIGLU, ALIGNED>(a, s);
+    case EPI_STORE: return gemm_instance<BM, BN, WM, WN, EPI_STORE, ALIGNED>(a, s);
+    case EPI_GATED_TO_F32: return gemm_instance<BM, BN, WM, WN, EPI_GATED_TO_F32, ALIGNED>(a, s);
+    case EPI_GATED_F32_IN: return gemm_instance<BM, BN, WM, WN, EPI_GATED_F32_IN, ALIGNED>(a, s);
+    case EPI_SWIGLU: return gemm_instance<BM, BN, WM, WN, EPI_SWIGLU, ALIGNED>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -266,6 +305,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if ((a.ldc & 3) != 0) return hipErrorInvalidValue;
   const bool gated = a.epilogue == EPI_GATED_TO_F32 || a.epilogue == EPI_GATED_F32_IN;
   if (gated && ((a.N & 3) != 0 || (a.ldr & 3) != 0)) return hipErrorInvalidValue;
+  // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
+  const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
+  if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)a.rows.seq_pad * a.lda * 2 >= (int64_t)kOob)
+    return hipErrorInvalidValue;
   const bool aligned = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&
                        ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
                        ((reinterpret_cast<uintptr_t>(a.W) & 15) == 0);
@@ -273,9 +316,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const long tiles_big = (long)((a.rows.n_valid + 255) / 256) * ((a.N + out_big - 1) / out_big);
   const bool big = tiles_big >= 512;
   if (aligned) {
-    return big ? gemm_dispatch_epi<256, 256, true>(a, s) : gemm_dispatch_epi<128, 128, true>(a, s);
+    // 256 x 256 tiles over 8 waves (two per SIMD, 128 x 64 accumulators each) measured faster
+    // than 4 waves of 128 x 128 at every projection of the 32k-token block.
+    if (big) return gemm_dispatch_epi<256, 256, 2, 4, true>(a, s);
+    return gemm_dispatch_epi<128, 128, 2, 2, true>(a, s);
   }
-  return gemm_dispatch_epi<128, 128, false>(a, s);
+  return gemm_dispatch_epi<128, 128, 2, 2, false>(a, s);
 }
 
 }  // namespace avdit

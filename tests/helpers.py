@@ -31,11 +31,26 @@ def close_stats(got, ref):
     return err, rms, cos
 
 
-def assert_close(got, ref, name: str, rel=REL_MAX_ERR, min_cos=MIN_COSINE):
+def bf16_floor(ref) -> float:
+    """max |bf16(ref) - ref|: the error of the exact result correctly rounded to bf16, the
+    smallest max error any bf16 output can have."""
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(O.bf16_round(ref) - ref))) if ref.size else 0.0
+
+
+def assert_close(got, ref, name: str, rel=REL_MAX_ERR, min_cos=MIN_COSINE, bf16_out=True):
+    """Floating-point parity bar for block outputs and loop latents: max |err| <= 2e-2 * RMS(ref)
+    and cosine >= 0.9995. For a bf16 output whose exact value, correctly rounded to bf16,
+    already exceeds 2e-2 * RMS (heavy-tailed outputs: half an ulp at max |ref| is larger than
+    2e-2 * RMS once max |ref| > ~5 RMS), the max-error bound is twice that rounding floor."""
     err, rms, cos = close_stats(got, ref)
-    say(f"  {name}: max|err| {err:.3e}  RMS(ref) {rms:.3e}  ratio {err / max(rms, 1e-30):.2e}  cos {cos:.7f}")
+    floor = bf16_floor(ref) if bf16_out else 0.0
+    bound = max(rel * rms, 2.0 * floor)
+    which = "2e-2*RMS" if bound == rel * rms else "2*bf16 floor"
+    say(f"  {name}: max|err| {err:.3e}  RMS(ref) {rms:.3e}  ratio {err / max(rms, 1e-30):.2e}  "
+        f"bf16 floor {floor / max(rms, 1e-30):.2e}*RMS  bound {which}  cos {cos:.7f}")
     assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
-    assert err <= rel * rms, f"{name}: max|err| {err:.3e} > {rel} * RMS {rms:.3e}"
+    assert err <= bound, f"{name}: max|err| {err:.3e} > bound {bound:.3e} ({which})"
     assert cos >= min_cos, f"{name}: cosine {cos:.7f} < {min_cos}"
     return err / max(rms, 1e-30), cos
 
