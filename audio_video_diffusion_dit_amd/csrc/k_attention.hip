@@ -3,7 +3,8 @@
 // zero-tail merge).
 //
 // Design for gfx950:
-//  * A workgroup (4 wave64s) owns 128 queries of one (request, head); each wave owns 32 queries
+//  * A workgroup (4 wave64s) owns 128 queries of one (request, head); workgroups are remapped so
+//    that the query tiles of one head run on one XCD (K/V fetched once per head). Each wave owns 32 queries
 //    and keeps its Q fragments in registers for the whole key sweep. Two workgroups share a CU,
 //    so one wave's softmax overlaps the other wave's matrix work on each SIMD.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (K tile from
@@ -101,9 +102,19 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int wave = tid >> 6;
-  const int bq = blockIdx.z;
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * kQB;
+  // Workgroup ids are dealt round-robin over the 8 XCDs; remap them so that each XCD receives a
+  // contiguous range of (request, head, query-tile) triples, query tile fastest: the query
+  // tiles of one head then run on one XCD and share its K/V tiles in that XCD's L2.
+  const int n_qt = gridDim.x;
+  const int total = gridDim.x * gridDim.y * gridDim.z;
+  const int b_lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = b_lin & 7, local = b_lin >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+  const int qt = logical % n_qt;
+  const int head = (logical / n_qt) % gridDim.y;
+  const int bq = logical / (n_qt * gridDim.y);
+  const int q0 = qt * kQB;
   const int V = a.valid[bq];
   const int L = a.seq_pad;
 

@@ -14,11 +14,17 @@ with HIP events on the stream it runs on over repeated launches on the block's o
 layout; useful FLOPs 4 V^2 D per launch against the 2.5 PFLOP/s dense bf16 MFMA peak.
 cpu_baseline: the float64 oracle on the host cores, one block of the same workload with a
 sample of output rows (keys/values for every valid row), in the same useful-FLOP unit.
+roofline.traffic: HBM bytes per attention launch from the committed counter summary
+profiles/k_attn_traffic.json (FETCH_SIZE and WRITE_SIZE, scaled by the same counters on a
+1 GiB device copy), reported only while that summary's recorded source hash matches the
+current attention kernel source; otherwise null.
 
-Prints ONE JSON line.
+Prints ONE JSON line. --roofline-only runs just one block, the attention timing and the copy
+used to calibrate the traffic counters (the command the counter runs profile).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,7 +47,28 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-off", action="store_true", help="skip the cache-off loop")
+    p.add_argument("--roofline-only", action="store_true",
+                   help="one block, the attention timing and the counter-calibration copy only")
     return p.parse_args()
+
+
+ATTN_SRC = os.path.join(ROOT, "audio_video_diffusion_dit_amd", "csrc", "k_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_traffic.json")
+
+
+def stored_traffic():
+    """Bytes per attention launch from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(ATTN_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sha:
+        return None
+    return t.get("bytes_per_launch")
 
 
 def log(msg):
@@ -93,55 +120,61 @@ def main():
     torch.cuda.set_device(0)
     wl = I.WORKLOADS[args.workload]
     log(f"[bench] generating {wl.name} inputs")
-    case = I.loop_case(wl, seed=0)
+    if args.roofline_only:
+        case = I.loop_case(wl, seed=0, n_blocks=1, n_intervals=2)
+    else:
+        case = I.loop_case(wl, seed=0)
     dims, lay = dev.dims_of(wl), dev.layout_of(wl)
     blocks = dev.upload_blocks(case.blocks)
     bw = [b.weights for b in blocks]
     temb = dev.to_dev_f32(case.temb_steps)
     x0 = dev.to_dev_f32(case.x0)
     x = torch.empty_like(x0)
-    ws, wmap = dev.workspace(dims, lay, len(blocks))
     n = wl.n_intervals
     stream = torch.cuda.current_stream()
-    pol_c = N.make_policy("conservative")
-    pol_o = N.make_policy("off")
     per_block = 8.0 * wl.n_valid * wl.hidden ** 2 + 6.0 * wl.n_valid * wl.hidden * wl.ffn + \
         4.0 * float(wl.n_valid) ** 2 * wl.hidden
 
-    def run(pol):
-        x.copy_(x0)
-        return N.denoise_loop(dims, lay, bw, n, case.sigmas_video, case.sigmas_audio, temb, pol, x,
-                              N.DIT_ATTN_VALID_ONLY, ws, stream=stream, want_hits=False)[0]
+    t_c = t_o = flops_c = flops_o = None
+    calls = hits = None
+    if not args.roofline_only:
+        ws, _ = dev.workspace(dims, lay, len(blocks))
+        pol_c = N.make_policy("conservative")
+        pol_o = N.make_policy("off")
 
-    log(f"[bench] warmup x{args.warmup}")
-    for _ in range(args.warmup):
-        run(pol_c)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} conservative loops")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        st = run(pol_c)
-    torch.cuda.synchronize()
-    t_c = (time.perf_counter() - t0) / args.steps
-    flops_c = st.useful_flops
-    assert abs(flops_c - st.executed_blocks * per_block) <= 1e-6 * flops_c
-    calls, hits = st.dit_calls, st.cache_hits
-    log(f"[bench] conservative: {t_c:.3f} s/loop, {flops_c / t_c / 1e12:.1f} TFLOP/s")
+        def run(pol):
+            x.copy_(x0)
+            return N.denoise_loop(dims, lay, bw, n, case.sigmas_video, case.sigmas_audio, temb,
+                                  pol, x, N.DIT_ATTN_VALID_ONLY, ws, stream=stream,
+                                  want_hits=False)[0]
 
-    t_o = flops_o = None
-    if not args.no_off:
+        log(f"[bench] warmup x{args.warmup}")
+        for _ in range(args.warmup):
+            run(pol_c)
         torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} conservative loops")
         t0 = time.perf_counter()
-        so = run(pol_o)
+        for _ in range(args.steps):
+            st = run(pol_c)
         torch.cuda.synchronize()
-        t_o = time.perf_counter() - t0
-        flops_o = so.useful_flops
-        log(f"[bench] off: {t_o:.3f} s/loop, {flops_o / t_o / 1e12:.1f} TFLOP/s")
+        t_c = (time.perf_counter() - t0) / args.steps
+        flops_c = st.useful_flops
+        assert abs(flops_c - st.executed_blocks * per_block) <= 1e-6 * flops_c
+        calls, hits = st.dit_calls, st.cache_hits
+        log(f"[bench] conservative: {t_c:.3f} s/loop, {flops_c / t_c / 1e12:.1f} TFLOP/s")
+        if not args.no_off:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            so = run(pol_o)
+            torch.cuda.synchronize()
+            t_o = time.perf_counter() - t0
+            flops_o = so.useful_flops
+            log(f"[bench] off: {t_o:.3f} s/loop, {flops_o / t_o / 1e12:.1f} TFLOP/s")
+        del ws
 
     # roofline: the attention kernel on the block's own qkv layout (filled by one block call)
     D, L, H, Dh = wl.hidden, wl.seq_pad, wl.heads, wl.head_dim
-    xin = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
-    xin.copy_(x0.to(torch.bfloat16))
+    xin = x0.to(torch.bfloat16)
     xout = torch.empty_like(xin)
     ws0, m0 = dev.workspace(dims, lay, 0)
     N.dit_block_forward(dims, lay, bw[0], temb[0], xin, xout, N.DIT_ATTN_VALID_ONLY, ws0, stream=stream)
@@ -163,20 +196,27 @@ def main():
     attn_flops = 4.0 * float(wl.n_valid) ** 2 * D
     achieved = attn_flops / t_attn / 1e12
     log(f"[bench] attention kernel: {t_attn * 1e3:.3f} ms, {achieved:.1f} TFLOP/s")
+    if args.roofline_only:
+        # plain device copy of 1 GiB: calibrates FETCH_SIZE / WRITE_SIZE for the traffic figure
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.roofline_only:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(case, args.cpu_rows)
 
     out = {
         "metric": METRIC,
-        "value": round(flops_c / t_c / 1e12, 2),
+        "value": round(flops_c / t_c / 1e12, 2) if t_c else None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(t_c * 1e3, 2),
+        "ms_per_step": round(t_c * 1e3, 2) if t_c else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -186,14 +226,15 @@ def main():
                    "n_video": wl.n_video, "n_audio": wl.n_audio, "seq_pad": L,
                    "blocks": wl.n_blocks, "intervals": n, "cache": "conservative",
                    "global_batch": 1, "seq_len": wl.n_valid, "parallelism": "single GPU"},
-        "steps_per_sec_conservative": round(n / t_c, 3),
+        "steps_per_sec_conservative": round(n / t_c, 3) if t_c else None,
         "steps_per_sec_off": round(n / t_o, 3) if t_o else None,
         "tflops_off": round(flops_o / t_o / 1e12, 2) if t_o else None,
         "dit_calls": calls,
         "cache_hits": hits,
-        "roofline": {"kernel": "k_attn<128> (valid-only attention)", "bound": "mfma",
+        "roofline": {"kernel": "avdit::k_attn<128> (valid-only attention, 4 V^2 D flop/launch)",
+                     "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(),
                      "launch_ms": round(t_attn * 1e3, 4)},
         "cpu_baseline": cpu,
     }

@@ -98,3 +98,25 @@ def test_attention_deterministic(N):
     a = _run(N, q, k, v, valid, N.DIT_ATTN_VALID_ONLY)
     b = _run(N, q, k, v, valid, N.DIT_ATTN_VALID_ONLY)
     assert np.array_equal(a, b)
+
+
+def test_attention_ragged_batch_full_size(N):
+    """4 packed requests of 16 heads x 128 in 8192-token buffers with valid lengths
+    {3000, 5100, 7777, 8192}: both modes bitwise equal, tails exactly zero, and 24 sampled
+    query rows per request (including each request's first and last valid row) against the
+    oracle."""
+    import oracle as O
+    from audio_video_diffusion_dit_amd.inputs import ATTN_RAGGED, attention_case, bf16_to_f32
+    cfg = ATTN_RAGGED
+    B, L, H, Dh, valid = cfg["batch"], cfg["seq_pad"], cfg["heads"], cfg["head_dim"], cfg["valid"]
+    say(f"attention ragged batch: B={B} L={L} H={H}x{Dh} valid={valid}")
+    q, k, v = attention_case(B, L, H, Dh, valid, seed=0)
+    vo = _run(N, q, k, v, valid, N.DIT_ATTN_VALID_ONLY, o_fill=0x7FC0)
+    fv = _run(N, q, k, v, valid, N.DIT_ATTN_FIXED_VALID, o_fill=0x7FC0)
+    assert np.array_equal(vo, fv), "fixed-valid and valid-only must agree bit for bit"
+    rng = np.random.default_rng(9)
+    for b, n in enumerate(valid):
+        assert np.all(vo[b, n:] == 0)
+        rows = np.sort(np.concatenate([rng.choice(n, 22, replace=False), [0, n - 1]]))
+        ref = O.attention_rows(bf16_to_f32(q[b, rows]), bf16_to_f32(k[b]), bf16_to_f32(v[b]), n)
+        assert_close(bf16_to_f32(vo[b, rows]), ref, f"request {b} (valid {n}), sampled rows")
