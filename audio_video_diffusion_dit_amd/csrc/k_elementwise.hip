@@ -11,12 +11,57 @@ namespace avdit {
 // ---------------------------------------------------------------------------------------
 // RMSNorm fused with indexed AdaLN modulation (TeleFuser PR #38, section 2; TeleFuser PR #23,
 // "Changes Made": indexed modulation). The input is the bf16 block input (norm1) or the fp32
-// mid-block residual (norm2). One wave owns a run of ROWS_PER_WAVE consecutive
-// rows; the modulation of the current modality, folded to mul = g * (1 + scale) and
-// add = shift, stays in registers and is reloaded only when the run crosses the
-// video/audio boundary, so the tables cost almost no cache traffic per row.
+// mid-block residual (norm2). One wave owns a run of 8 consecutive rows and keeps the next
+// row's loads in flight while it reduces the current one; the modulation of the current
+// modality, folded to mul = g * (1 + scale) and add = shift, stays in registers and is
+// reloaded only when the run crosses the video/audio boundary, so the tables cost almost no
+// cache traffic per row.
 // ---------------------------------------------------------------------------------------
 constexpr int kNormRowsPerWave = 8;
+
+// Row data as loaded: 8 elements per chunk, bf16 (one 16-byte word) or fp32 (two).
+template <bool F32IN>
+struct RowChunk {
+  uint4 w[F32IN ? 2 : 1];
+};
+
+template <int CPL, bool F32IN>
+__device__ __forceinline__ void load_row(const NormModArgs& a, int row, int lane, int nchunk,
+                                         RowChunk<F32IN> (&r)[CPL]) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+#pragma unroll
+    for (int h = 0; h < (F32IN ? 2 : 1); ++h) r[i].w[h] = zero4();
+    if (c < nchunk) {
+      if (F32IN) {
+        const uint4* in = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + (size_t)row * a.D);
+        r[i].w[0] = in[2 * c];
+        r[i].w[F32IN ? 1 : 0] = in[2 * c + 1];
+      } else {
+        const uint4* in = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)row * a.D);
+        r[i].w[0] = in[c];
+      }
+    }
+  }
+}
+
+template <bool F32IN>
+__device__ __forceinline__ void unpack_chunk(const RowChunk<F32IN>& r, float (&x)[8]) {
+  if (F32IN) {
+    const uint32_t w[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w,
+                           r.w[F32IN ? 1 : 0].x, r.w[F32IN ? 1 : 0].y, r.w[F32IN ? 1 : 0].z, r.w[F32IN ? 1 : 0].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
+  } else {
+    const uint32_t w[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf_lo(w[j]);
+      x[2 * j + 1] = bf_hi(w[j]);
+    }
+  }
+}
 
 template <int CPL, bool F32IN>  // CPL: 8-element chunks per lane, ceil(D / 512)
 __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
@@ -28,10 +73,17 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
   float mul[CPL][8];
   float add[CPL][8];
   int cur = -1;
+  const int row0 = wave * kNormRowsPerWave;
+  if (row0 >= a.rows.seq_pad) return;
 
+  // software pipeline: the next row's loads are in flight while the current row is reduced
+  RowChunk<F32IN> buf[CPL], nxt[CPL];
+  if (row0 < a.rows.n_valid) load_row<CPL, F32IN>(a, row0, lane, nchunk, buf);
   for (int rr = 0; rr < kNormRowsPerWave; ++rr) {
-    const int row = wave * kNormRowsPerWave + rr;
+    const int row = row0 + rr;
     if (row >= a.rows.seq_pad) return;
+    if (rr + 1 < kNormRowsPerWave && row + 1 < a.rows.n_valid)
+      load_row<CPL, F32IN>(a, row + 1, lane, nchunk, nxt);
     uint4* out = reinterpret_cast<uint4*>(a.h + (size_t)row * D);
     if (row >= a.rows.n_valid) {
 #pragma unroll
@@ -39,78 +91,65 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
         const int c = lane + 64 * i;
         if (c < nchunk) out[c] = zero4();
       }
-      continue;
-    }
-    const int m = row < a.rows.n_video ? 0 : 1;
-    if (m != cur) {
-      cur = m;
-      const float* A = a.ada + (size_t)m * 6 * D;
-      const float* T = a.temb + (size_t)m * 6 * D;
+    } else {
+      const int m = row < a.rows.n_video ? 0 : 1;
+      if (m != cur) {
+        cur = m;
+        const float* A = a.ada + (size_t)m * 6 * D;
+        const float* T = a.temb + (size_t)m * 6 * D;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = lane + 64 * i;
+          if (c < nchunk) {
+            const int d0 = c * 8;
+#pragma unroll
+            for (int e = 0; e < 8; e += 4) {
+              const float4 g = *reinterpret_cast<const float4*>(a.gain + d0 + e);
+              const float4 sa = *reinterpret_cast<const float4*>(A + a.scale_chunk * D + d0 + e);
+              const float4 st = *reinterpret_cast<const float4*>(T + a.scale_chunk * D + d0 + e);
+              const float4 ha = *reinterpret_cast<const float4*>(A + a.shift_chunk * D + d0 + e);
+              const float4 ht = *reinterpret_cast<const float4*>(T + a.shift_chunk * D + d0 + e);
+              mul[i][e + 0] = g.x * (1.0f + (sa.x + st.x));
+              mul[i][e + 1] = g.y * (1.0f + (sa.y + st.y));
+              mul[i][e + 2] = g.z * (1.0f + (sa.z + st.z));
+              mul[i][e + 3] = g.w * (1.0f + (sa.w + st.w));
+              add[i][e + 0] = ha.x + ht.x;
+              add[i][e + 1] = ha.y + ht.y;
+              add[i][e + 2] = ha.z + ht.z;
+              add[i][e + 3] = ha.w + ht.w;
+            }
+          }
+        }
+      }
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        float x[8];
+        unpack_chunk<F32IN>(buf[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+      }
+      ss = wave_sum(ss);
+      const float r = rsqrtf(ss * inv_d + a.eps);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
         if (c < nchunk) {
-          const int d0 = c * 8;
+          float x[8];
+          unpack_chunk<F32IN>(buf[i], x);
+          uint32_t o[4];
 #pragma unroll
-          for (int e = 0; e < 8; e += 4) {
-            const float4 g = *reinterpret_cast<const float4*>(a.gain + d0 + e);
-            const float4 sa = *reinterpret_cast<const float4*>(A + a.scale_chunk * D + d0 + e);
-            const float4 st = *reinterpret_cast<const float4*>(T + a.scale_chunk * D + d0 + e);
-            const float4 ha = *reinterpret_cast<const float4*>(A + a.shift_chunk * D + d0 + e);
-            const float4 ht = *reinterpret_cast<const float4*>(T + a.shift_chunk * D + d0 + e);
-            mul[i][e + 0] = g.x * (1.0f + (sa.x + st.x));
-            mul[i][e + 1] = g.y * (1.0f + (sa.y + st.y));
-            mul[i][e + 2] = g.z * (1.0f + (sa.z + st.z));
-            mul[i][e + 3] = g.w * (1.0f + (sa.w + st.w));
-            add[i][e + 0] = ha.x + ht.x;
-            add[i][e + 1] = ha.y + ht.y;
-            add[i][e + 2] = ha.z + ht.z;
-            add[i][e + 3] = ha.w + ht.w;
+          for (int j = 0; j < 4; ++j) {
+            const float y0 = fmaf(x[2 * j] * r, mul[i][2 * j], add[i][2 * j]);
+            const float y1 = fmaf(x[2 * j + 1] * r, mul[i][2 * j + 1], add[i][2 * j + 1]);
+            o[j] = pack_bf16x2(y0, y1);
           }
+          out[c] = make_uint4(o[0], o[1], o[2], o[3]);
         }
       }
     }
-    // 8 elements per chunk, held as fp32
-    float xv[CPL][8];
-    float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane + 64 * i;
-      if (F32IN) {
-        const float4* in = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)row * D);
-        const float4 p0 = c < nchunk ? in[2 * c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 p1 = c < nchunk ? in[2 * c + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-        xv[i][0] = p0.x; xv[i][1] = p0.y; xv[i][2] = p0.z; xv[i][3] = p0.w;
-        xv[i][4] = p1.x; xv[i][5] = p1.y; xv[i][6] = p1.z; xv[i][7] = p1.w;
-      } else {
-        const uint4* in = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)row * D);
-        const uint4 v = c < nchunk ? in[c] : zero4();
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xv[i][2 * j] = bf_lo(w[j]);
-          xv[i][2 * j + 1] = bf_hi(w[j]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(xv[i][e], xv[i][e], ss);
-    }
-    ss = wave_sum(ss);
-    const float r = rsqrtf(ss * inv_d + a.eps);
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nchunk) {
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float y0 = fmaf(xv[i][2 * j] * r, mul[i][2 * j], add[i][2 * j]);
-          const float y1 = fmaf(xv[i][2 * j + 1] * r, mul[i][2 * j + 1], add[i][2 * j + 1]);
-          o[j] = pack_bf16x2(y0, y1);
-        }
-        out[c] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    }
+    for (int i = 0; i < CPL; ++i) buf[i] = nxt[i];
   }
 }
 
@@ -182,7 +221,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
   uint16_t* base = a.qkv + (size_t)token * a.row_stride + gl * 8;
   const int nvec = 2 * a.heads;
 
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int v0 = 0; v0 < nvec; v0 += U) {
     uint4 raw[U];
 #pragma unroll
