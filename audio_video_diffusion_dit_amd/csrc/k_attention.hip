@@ -9,7 +9,7 @@
 //    so one wave's softmax overlaps the other wave's matrix work on each SIMD.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (K tile from
 //    LDS as the A operand, Q as the B operand): each lane then holds 32 of the 64 scores of
-//    one query per key tile, so the running max needs one cross-lane exchange (lanes l, l^32).
+//    one query per key tile, so the running max needs one cross-lane exchange (lanes l, l^32: one v_permlane32_swap).
 //  * O^T = V^T P^T reuses the score registers directly as the B operand: the k index of that
 //    MFMA is mapped onto keys in the order the score layout already has. V stays row-major in
 //    LDS, like K, and its A-operand fragments are assembled by the LDS transpose read
@@ -85,6 +85,17 @@ __device__ __forceinline__ void dma_b128(uint32_t lds_base, uint32_t voffset, i3
                : "memory", "m0");
 }
 
+// Max and sum of the values of lanes l and l ^ 32, from one v_permlane32_swap (no LDS round
+// trip): the swap leaves lanes l and l + 32 holding {x[l], x[l + 32]} in its two results.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int DH>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int NC = DH / 8;          // 16-byte chunks per K/V row
@@ -141,6 +152,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     if (my_q < V) w = *reinterpret_cast<const u32x4*>(Q + (int64_t)my_q * a.row_stride + (2 * s + hh) * 8);
     qf[s] = __builtin_bit_cast(bf16x8, w);
   }
+  // Consume the Q fragments once here: the compiler then places its wait for these loads before
+  // the key loop instead of at their first use inside it, where the same counter would also
+  // wait for the K/V prefetch in flight (the LDS-destination loads are invisible to it).
+#pragma unroll
+  for (int s = 0; s < QS; ++s) asm volatile("" ::"v"(qf[s]));
 
   // ---- global -> LDS staging: wave w's i-th load fills 16-byte slots (4 i + w) * 64 + lane of
   // a tile, i.e. row p / NC and physical chunk p % NC of slot p; the lane fetches the logical
@@ -253,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = pair_max(mx);
     // The running max is exact (the largest probability of a row is exactly 1). The
     // accumulator rescale is skipped when no lane's max grew: alpha would be exactly 1.
     const float m_new = fmaxf(m_run, mx);
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   }
 
   // ---- normalise and store: element (j, i) of oacc[t] is d = 32 t + 8 j + 4 hh + i ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   const float inv_l = 1.0f / l_tot;
   if (my_q < L) {
     uint16_t* orow = O + (int64_t)my_q * a.o_row_stride;
