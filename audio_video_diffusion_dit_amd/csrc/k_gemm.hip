@@ -31,6 +31,8 @@ namespace avdit {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 constexpr int kBK = 64;                      // k-tile; 8 chunks of 8 bf16 per LDS row
 constexpr uint32_t kOob = 0x80000000u;       // buffer offset past every range: reads zero
@@ -65,6 +67,97 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
+// Tile selection: workgroup ids are dealt round-robin over the 8 XCDs; each XCD receives a
+// contiguous range of tiles, ordered in groups of 8 token-tiles, so that the workgroups resident
+// on one XCD share operand panels in its L2.
+__device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_m, int& tile_n) {
+  const int nt = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = nt >> 3, rem = nt & 7;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+  constexpr int GM = 8;
+  const int group = logical / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int in_group = logical - group * GM * tiles_n;
+  tile_m = first_m + in_group % gm;
+  tile_n = in_group / gm;
+}
+
+// Fused epilogue of one wave's accumulator block: lane (l32, hh) holds features fb..fb+3 of
+// token m0 + wm TM + 32 t + l32 in acc[f][t][4 j .. 4 j + 3], fb = n0 + wn (OUT_T 32) + 32 f +
+// 8 j + 4 hh (SwiGLU pairs gate sub-tile 2 f with up sub-tile 2 f + 1). Rows at or past n_valid
+// are written 0, rows past seq_pad are not written.
+template <int EPI, int FT, int MT, int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][MT], int m0, int n0,
+                                           int wm, int wn, int lane) {
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int n_valid = a.rows.n_valid;
+  const int seq_pad = a.rows.seq_pad;
+  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int tok = m0 + wm * TM + t * 32 + l32;
+    if (tok >= seq_pad) continue;
+    const bool valid = tok < n_valid;
+    const int mod = tok < a.rows.n_video ? 0 : 1;
+    constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
+#pragma unroll
+    for (int f = 0; f < OUT_T; ++f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int fb = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
+        if (fb >= a.N) continue;
+        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (valid) {
+          if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              o[i] = silu_mul(acc[2 * f][t][4 * j + i], acc[2 * f + 1][t][4 * j + i]);
+          } else if constexpr (GATED) {
+            float r[4];
+            if constexpr (EPI == EPI_GATED_TO_F32) {
+              const u32x2 rr = *reinterpret_cast<const u32x2*>(
+                  static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fb);
+              r[0] = bf_lo(rr.x); r[1] = bf_hi(rr.x); r[2] = bf_lo(rr.y); r[3] = bf_hi(rr.y);
+            } else {
+              const float4 rr = *reinterpret_cast<const float4*>(
+                  static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
+              r[0] = rr.x; r[1] = rr.y; r[2] = rr.z; r[3] = rr.w;
+            }
+            const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
+            const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
+            const float4 gt = *reinterpret_cast<const float4*>(a.temb + goff);
+            o[0] = fmaf(ga.x + gt.x, acc[f][t][4 * j + 0], r[0]);
+            o[1] = fmaf(ga.y + gt.y, acc[f][t][4 * j + 1], r[1]);
+            o[2] = fmaf(ga.z + gt.z, acc[f][t][4 * j + 2], r[2]);
+            o[3] = fmaf(ga.w + gt.w, acc[f][t][4 * j + 3], r[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
+          }
+        }
+        if constexpr (EPI == EPI_GATED_TO_F32) {
+          float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
+          *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
+          if (fb + 4 <= a.N) {
+            *reinterpret_cast<u32x2*>(crow + fb) =
+                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (fb + i < a.N) crow[fb + i] = to_bf16(o[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_m, int tiles_n) {
   constexpr int NT = 64 * WM * WN;    // threads
@@ -88,19 +181,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
   const int wm = wave % WM;   // token slice
   const int wn = wave / WM;   // feature slice
 
-  // ---- tile selection: XCD-contiguous ranges, grouped token-tile order ----
-  const int nt = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3;
-  const int per = nt >> 3, rem = nt & 7;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
-  constexpr int GM = 8;
-  const int group = logical / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-  const int in_group = logical - group * GM * tiles_n;
-  const int tile_m = first_m + in_group % gm;
-  const int tile_n = in_group / gm;
+  int tile_m, tile_n;
+  select_tile(tiles_m, tiles_n, tile_m, tile_n);
 
   const int m0 = tile_m * BM;
   const int n_valid = a.rows.n_valid;
@@ -213,67 +295,178 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
     }
   }
 
-  // ---- epilogue: lane holds features fb..fb+3 of token `tok` for each (f, t, j) ----
-  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN);
+  store_tile<EPI, FT, MT, TM, TN>(a, acc, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Large-problem GEMM: operands go straight from memory into a ring of LDS stages.
+//
+//  * 256 x 256 tiles (weights x tokens), 8 wave64s of 64 features x 128 tokens, k-tiles of 32.
+//  * Buffer loads with the LDS destination (no staging registers, no LDS write instructions):
+//    one wave load fills 16 LDS rows of 64 bytes; each lane fetches the 16-byte global chunk
+//    that the swizzle places in its slot. Loads run up to STAGES - 1 k-tiles ahead of the MFMAs.
+//  * The barrier that publishes k-tile kt + 1 sits between the two MFMA k-steps of k-tile kt,
+//    so the first fragments of kt + 1 are read from LDS while the second k-step's MFMAs run.
+//    At that barrier every wave has finished reading k-tile kt - 1, whose stage then receives
+//    the loads of k-tile kt + STAGES - 1.
+//  * LDS rows are 64 bytes with the chunk index XOR-swizzled by (r >> 2) & 3: the 16 rows that
+//    one group of lanes reads at a logical chunk fall on 16 distinct 16-byte bank groups.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDlBK = 32;                  // k-tile
+constexpr int kDlStages = 4;               // LDS ring depth (128 KB); 3 measured slower, 5 equal
+constexpr int kDlRows = 512;               // LDS rows per stage: 256 weight rows, 256 token rows
+constexpr int kDlStageBytes = kDlRows * 64;
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t ad = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int32_t)(uint32_t)ad, (int32_t)(uint32_t)(ad >> 32), (int32_t)bytes, kRsrcWord3};
+}
+
+// 16 bytes per lane from memory into LDS at lds_base + 16 lane (lds_base wave-uniform); offsets
+// past the resource range read as zero. Completion is awaited with explicit vmcnt waits.
+__device__ __forceinline__ void dl_b128(uint32_t lds_base, uint32_t voffset, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
+
+template <int EPI>
+__global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+  constexpr int STAGES = kDlStages;
+  constexpr int NW = WM * WN;         // waves
+  constexpr int LPW = 32 / NW;        // 16-row wave loads per wave per stage
+  constexpr int TM = BM / WM;         // 128 tokens per wave
+  constexpr int TN = BN / WN;         // 64 weight rows per wave
+  constexpr int MT = TM / 32;
+  constexpr int FT = TN / 32;
+  static_assert(EPI != EPI_SWIGLU || (FT % 2) == 0, "SwiGLU pairs gate/up sub-tiles");
+
+  __shared__ u32x4 lds_ring[STAGES * kDlRows * 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int wave = tid >> 6;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+
+  int tile_m, tile_n;
+  select_tile(tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM;
+  const int n_valid = a.rows.n_valid;
+  const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
+
+  f32x16 acc[FT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int tok = m0 + wm * TM + t * 32 + l32;
-    if (tok >= seq_pad) continue;
-    const bool valid = tok < n_valid;
-    const int mod = tok < a.rows.n_video ? 0 : 1;
-    constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
+  for (int f = 0; f < FT; ++f)
 #pragma unroll
-    for (int f = 0; f < OUT_T; ++f) {
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int fb = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
-        if (fb >= a.N) continue;
-        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (valid) {
-          if constexpr (EPI == EPI_SWIGLU) {
+      for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.0f;
+
+  if (m0 < n_valid) {
+    const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
+    const i32x4 rs_w = raw_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
+    const i32x4 rs_a = raw_rsrc(a.A, (uint32_t)((int64_t)a.rows.seq_pad * a.lda * 2));
+    // Wave load i fills LDS rows 16 (NW i + wave) .. + 15 of a stage: the first LPW / 2 loads
+    // weight rows, the rest token rows. Lane: row + lane / 4, physical chunk lane % 4.
+    uint32_t goff[LPW];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              o[i] = silu_mul(acc[2 * f][t][4 * j + i], acc[2 * f + 1][t][4 * j + i]);
-          } else if constexpr (GATED) {
-            float r[4];
-            if constexpr (EPI == EPI_GATED_TO_F32) {
-              const u32x2 rr = *reinterpret_cast<const u32x2*>(
-                  static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fb);
-              r[0] = bf_lo(rr.x); r[1] = bf_hi(rr.x); r[2] = bf_lo(rr.y); r[3] = bf_hi(rr.y);
-            } else {
-              const float4 rr = *reinterpret_cast<const float4*>(
-                  static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
-              r[0] = rr.x; r[1] = rr.y; r[2] = rr.z; r[3] = rr.w;
-            }
-            const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
-            const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
-            const float4 gt = *reinterpret_cast<const float4*>(a.temb + goff);
-            o[0] = fmaf(ga.x + gt.x, acc[f][t][4 * j + 0], r[0]);
-            o[1] = fmaf(ga.y + gt.y, acc[f][t][4 * j + 1], r[1]);
-            o[2] = fmaf(ga.z + gt.z, acc[f][t][4 * j + 2], r[2]);
-            o[3] = fmaf(ga.w + gt.w, acc[f][t][4 * j + 3], r[3]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
-          }
-        }
-        if constexpr (EPI == EPI_GATED_TO_F32) {
-          float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
-          *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
+    for (int i = 0; i < LPW; ++i) {
+      const int r = 16 * (NW * i + wave) + (lane >> 2);
+      const int kc = (lane & 3) ^ dl_swz(r);
+      if (i < LPW / 2) {
+        int wrow, feat;
+        if (EPI == EPI_SWIGLU) {
+          const int blk = r >> 5;
+          feat = n0 + (blk >> 1) * 32 + (r & 31);
+          wrow = (blk & 1) ? a.up_offset + feat : feat;
         } else {
-          uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
-          if (fb + 4 <= a.N) {
-            *reinterpret_cast<u32x2*>(crow + fb) =
-                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (fb + i < a.N) crow[fb + i] = to_bf16(o[i]);
-          }
+          feat = n0 + r;
+          wrow = feat;
         }
+        goff[i] = feat < a.N ? (uint32_t)((int64_t)wrow * a.ldw * 2 + kc * 16) : kOob;
+      } else {
+        const int tok = m0 + (r - BN);
+        goff[i] = tok < n_valid ? (uint32_t)((int64_t)tok * a.lda * 2 + kc * 16) : kOob;
       }
     }
+    lds_char_t* lds = (lds_char_t*)(lds_ring);
+    const uint32_t lbase = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)lds + wave * 1024);
+    const int nk = a.K / kDlBK;
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      const uint32_t sb = lbase + (uint32_t)(kt % STAGES) * kDlStageBytes;
+      const uint32_t kb = (uint32_t)kt * (kDlBK * 2);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        dl_b128(sb + i * NW * 1024, goff[i] + kb, i < LPW / 2 ? rs_w : rs_a);
+    };
+    // Fragment of logical chunk 2 s + hh of LDS row `row` (row % 32 == l32).
+    const int sw = dl_swz(l32);
+    const int foff0 = l32 * 64 + ((0 + hh) ^ sw) * 16;
+    const int foff1 = l32 * 64 + ((2 + hh) ^ sw) * 16;
+    bf16x8 af[2][FT], bf[2][MT];
+    auto read_frags = [&](int kt, int s, int slot) __attribute__((always_inline)) {
+      lds_char_t* st = lds + (kt % STAGES) * kDlStageBytes + (s ? foff1 : foff0);
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+        af[slot][f] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<lds_u32x4_t*>(st + (wn * TN + f * 32) * 64));
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        bf[slot][t] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<lds_u32x4_t*>(st + (BN + wm * TM + t * 32) * 64));
+    };
+    auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][f], bf[slot][t], acc[f][t],
+                                                              0, 0, 0);
+    };
+    // wait until at most `ahead` k-tiles of this wave's loads (4 each) are still in flight
+    static_assert(LPW == 4 && STAGES >= 3 && STAGES <= 5, "vmcnt values encode 4 loads per tile");
+    auto wait_tiles = [&](int ahead) __attribute__((always_inline)) {
+      if (ahead >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else if (ahead == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    // Prologue: k-tiles 0 .. STAGES - 2 in flight, wait for k-tile 0.
+    for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
+    wait_tiles(min(STAGES - 2, nk - 1));
+    __syncthreads();
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      read_frags(kt, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs they overlap
+      mfmas(0);
+      // k-tile kt + 1 landed (this wave's part; the barrier covers the others), and every
+      // wave is done with k-tile kt - 1, whose stage receives k-tile kt + STAGES - 1. Issued
+      // so far: k-tiles up to min(kt + STAGES - 2, nk - 1).
+      wait_tiles(min(STAGES - 3, nk - 2 - kt));
+      __syncthreads();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      read_frags(kt + 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+    }
+    // last k-tile (peeled, so that the loop body has a single path through the barrier)
+    read_frags(nk - 1, 1, 1);
+    mfmas(0);
+    mfmas(1);
   }
+  store_tile<EPI, FT, MT, TM, TN>(a, acc, m0, n0, wm, wn, lane);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
@@ -315,6 +508,19 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const int out_big = (a.epilogue == EPI_SWIGLU) ? 128 : 256;
   const long tiles_big = (long)((a.rows.n_valid + 255) / 256) * ((a.N + out_big - 1) / out_big);
   const bool big = tiles_big >= 512;
+  if (aligned && big && (a.K % kDlBK) == 0) {
+    const int tiles_m = (a.rows.seq_pad + 255) / 256;
+    const int tiles_n = (a.N + out_big - 1) / out_big;
+    const dim3 grid(tiles_m * tiles_n), block(512);
+    switch (a.epilogue) {
+      case EPI_STORE: hipLaunchKernelGGL(k_gemm_dl<EPI_STORE>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      case EPI_GATED_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      case EPI_GATED_F32_IN: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_IN>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_dl<EPI_SWIGLU>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (aligned) {
     // 256 x 256 tiles over 8 waves (two per SIMD, 128 x 64 accumulators each) measured faster
     // than 4 waves of 128 x 128 at every projection of the 32k-token block.
