@@ -301,21 +301,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
 // ---------------------------------------------------------------------------------------------
 // Large-problem GEMM: operands go straight from memory into a ring of LDS stages.
 //
-//  * 256 x 256 tiles (weights x tokens), 8 wave64s of 64 features x 128 tokens, k-tiles of 32.
+//  * 256 x 256 tiles (weights x tokens), 8 wave64s of 64 features x 128 tokens, k-tiles of 64.
 //  * Buffer loads with the LDS destination (no staging registers, no LDS write instructions):
-//    one wave load fills 16 LDS rows of 64 bytes; each lane fetches the 16-byte global chunk
-//    that the swizzle places in its slot. Loads run up to STAGES - 1 k-tiles ahead of the MFMAs.
-//  * The barrier that publishes k-tile kt + 1 sits between the two MFMA k-steps of k-tile kt,
-//    so the first fragments of kt + 1 are read from LDS while the second k-step's MFMAs run.
-//    At that barrier every wave has finished reading k-tile kt - 1, whose stage then receives
-//    the loads of k-tile kt + STAGES - 1.
-//  * LDS rows are 64 bytes with the chunk index XOR-swizzled by (r >> 2) & 3: the 16 rows that
-//    one group of lanes reads at a logical chunk fall on 16 distinct 16-byte bank groups.
+//    one wave load fills 8 LDS rows of 128 bytes; each lane fetches the 16-byte global chunk
+//    that the swizzle places in its slot.
+//  * One barrier per k-tile, placed before the last MFMA k-step of k-tile kt: by then every
+//    fragment of kt is in registers, so kt's stage receives the loads of k-tile kt + 2 while
+//    the barrier publishes k-tile kt + 1, whose first fragments are read under the last
+//    k-step's MFMAs. Two 64 KB stages measured faster than four 32 KB ones (half the barriers;
+//    deeper prefetch gained nothing).
 // ---------------------------------------------------------------------------------------------
-constexpr int kDlBK = 32;                  // k-tile
-constexpr int kDlStages = 4;               // LDS ring depth (128 KB); 3 measured slower, 5 equal
+constexpr int kDlBK = 64;                  // k-tile
+constexpr int kDlStages = 2;               // LDS ring depth: 2 x 64 KB
 constexpr int kDlRows = 512;               // LDS rows per stage: 256 weight rows, 256 token rows
-constexpr int kDlStageBytes = kDlRows * 64;
+constexpr int kDlRowB = kDlBK * 2;         // bytes per LDS row
+constexpr int kDlNch = kDlBK / 8;          // 16-byte chunks per row
+constexpr int kDlStageBytes = kDlRows * kDlRowB;
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -323,7 +324,6 @@ __device__ __forceinline__ i32x4 raw_rsrc(const void* p, uint32_t bytes) {
   const uint64_t ad = reinterpret_cast<uint64_t>(p);
   return i32x4{(int32_t)(uint32_t)ad, (int32_t)(uint32_t)(ad >> 32), (int32_t)bytes, kRsrcWord3};
 }
-
 // 16 bytes per lane from memory into LDS at lds_base + 16 lane (lds_base wave-uniform); offsets
 // past the resource range read as zero. Completion is awaited with explicit vmcnt waits.
 __device__ __forceinline__ void dl_b128(uint32_t lds_base, uint32_t voffset, i32x4 rsrc) {
@@ -332,37 +332,27 @@ __device__ __forceinline__ void dl_b128(uint32_t lds_base, uint32_t voffset, i32
                : "s"(lds_base), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
-
-__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
+// Chunk swizzle of a 128-byte LDS row: the 16 rows that one group of lanes reads at a logical
+// chunk (8 even and 8 odd rows) land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int dl_swz(int r) { return (r >> 1) & 7; }
 
 template <int EPI>
 __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int tiles_n) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
   constexpr int STAGES = kDlStages;
-  constexpr int NW = WM * WN;         // waves
-  constexpr int LPW = 32 / NW;        // 16-row wave loads per wave per stage
-  constexpr int TM = BM / WM;         // 128 tokens per wave
-  constexpr int TN = BN / WN;         // 64 weight rows per wave
-  constexpr int MT = TM / 32;
-  constexpr int FT = TN / 32;
-  static_assert(EPI != EPI_SWIGLU || (FT % 2) == 0, "SwiGLU pairs gate/up sub-tiles");
-
-  __shared__ u32x4 lds_ring[STAGES * kDlRows * 4];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-  const int wave = tid >> 6;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-
+  constexpr int NW = WM * WN;
+  constexpr int LPW = 32 * kDlNch / 4 / NW;   // wave loads per wave per stage (= kDlNch)
+  constexpr int RPL = 64 / kDlNch;            // rows per wave load
+  constexpr int TM = BM / WM, TN = BN / WN, MT = TM / 32, FT = TN / 32;
+  constexpr int KS = kDlBK / 16;              // MFMA k-steps per k-tile
+  __shared__ u32x4 lds_ring[STAGES * kDlStageBytes / 16];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
   int tile_m, tile_n;
   select_tile(tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int n_valid = a.rows.n_valid;
   const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
-
   f32x16 acc[FT][MT];
 #pragma unroll
   for (int f = 0; f < FT; ++f)
@@ -370,18 +360,15 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.0f;
-
   if (m0 < n_valid) {
     const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
     const i32x4 rs_w = raw_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
     const i32x4 rs_a = raw_rsrc(a.A, (uint32_t)((int64_t)a.rows.seq_pad * a.lda * 2));
-    // Wave load i fills LDS rows 16 (NW i + wave) .. + 15 of a stage: the first LPW / 2 loads
-    // weight rows, the rest token rows. Lane: row + lane / 4, physical chunk lane % 4.
     uint32_t goff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int r = 16 * (NW * i + wave) + (lane >> 2);
-      const int kc = (lane & 3) ^ dl_swz(r);
+      const int r = RPL * (NW * i + wave) + lane / kDlNch;
+      const int kc = (lane % kDlNch) ^ dl_swz(r);
       if (i < LPW / 2) {
         int wrow, feat;
         if (EPI == EPI_SWIGLU) {
@@ -409,62 +396,59 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
       for (int i = 0; i < LPW; ++i)
         dl_b128(sb + i * NW * 1024, goff[i] + kb, i < LPW / 2 ? rs_w : rs_a);
     };
-    // Fragment of logical chunk 2 s + hh of LDS row `row` (row % 32 == l32).
     const int sw = dl_swz(l32);
-    const int foff0 = l32 * 64 + ((0 + hh) ^ sw) * 16;
-    const int foff1 = l32 * 64 + ((2 + hh) ^ sw) * 16;
+    int foff[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) foff[s] = l32 * kDlRowB + ((2 * s + hh) ^ sw) * 16;
     bf16x8 af[2][FT], bf[2][MT];
     auto read_frags = [&](int kt, int s, int slot) __attribute__((always_inline)) {
-      lds_char_t* st = lds + (kt % STAGES) * kDlStageBytes + (s ? foff1 : foff0);
+      lds_char_t* st = lds + (kt % STAGES) * kDlStageBytes + foff[s];
 #pragma unroll
       for (int f = 0; f < FT; ++f)
-        af[slot][f] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<lds_u32x4_t*>(st + (wn * TN + f * 32) * 64));
+        af[slot][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<lds_u32x4_t*>(st + (wn * TN + f * 32) * kDlRowB));
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        bf[slot][t] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<lds_u32x4_t*>(st + (BN + wm * TM + t * 32) * 64));
+        bf[slot][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<lds_u32x4_t*>(st + (BN + wm * TM + t * 32) * kDlRowB));
     };
     auto mfmas = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int f = 0; f < FT; ++f)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][f], bf[slot][t], acc[f][t],
-                                                              0, 0, 0);
+          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][f], bf[slot][t], acc[f][t], 0, 0, 0);
     };
-    // wait until at most `ahead` k-tiles of this wave's loads (4 each) are still in flight
-    static_assert(LPW == 4 && STAGES >= 3 && STAGES <= 5, "vmcnt values encode 4 loads per tile");
+    // wait until at most `ahead` k-tiles of this wave's loads (8 each) are still in flight
+    static_assert(LPW == 8 && STAGES == 2, "vmcnt values encode 8 loads per k-tile, 2 stages");
     auto wait_tiles = [&](int ahead) __attribute__((always_inline)) {
-      if (ahead >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else if (ahead == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if (ahead >= 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
-
-    // Prologue: k-tiles 0 .. STAGES - 2 in flight, wait for k-tile 0.
-    for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
-    wait_tiles(min(STAGES - 2, nk - 1));
+    // prologue: every stage filled, wait for k-tile 0
+    for (int kt = 0; kt < STAGES && kt < nk; ++kt) issue(kt);
+    wait_tiles(min(STAGES - 1, nk - 1));
     __syncthreads();
     read_frags(0, 0, 0);
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      read_frags(kt, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs they overlap
-      mfmas(0);
-      // k-tile kt + 1 landed (this wave's part; the barrier covers the others), and every
-      // wave is done with k-tile kt - 1, whose stage receives k-tile kt + STAGES - 1. Issued
-      // so far: k-tiles up to min(kt + STAGES - 2, nk - 1).
-      wait_tiles(min(STAGES - 3, nk - 2 - kt));
+#pragma unroll
+      for (int s = 0; s + 1 < KS; ++s) {
+        read_frags(kt, s + 1, (s + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(s & 1);
+      }
+      // all fragments of k-tile kt are in registers: its stage takes k-tile kt + STAGES
+      wait_tiles(min(STAGES - 2, nk - 2 - kt));
       __syncthreads();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      if (kt + STAGES < nk) issue(kt + STAGES);
       read_frags(kt + 1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(1);
+      mfmas((KS - 1) & 1);
     }
-    // last k-tile (peeled, so that the loop body has a single path through the barrier)
-    read_frags(nk - 1, 1, 1);
-    mfmas(0);
-    mfmas(1);
+#pragma unroll
+    for (int s = 0; s + 1 < KS; ++s) {
+      read_frags(nk - 1, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
+    }
+    mfmas((KS - 1) & 1);
   }
   store_tile<EPI, FT, MT, TM, TN>(a, acc, m0, n0, wm, wn, lane);
 }
