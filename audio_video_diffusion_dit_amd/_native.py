@@ -92,7 +92,7 @@ def _load():
     lib.dit_attention_forward.restype = c_int32
     lib.dit_attention_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                           c_int32, c_int32, c_int64, c_int64, c_int64, c_int64,
-                                          POINTER(c_int32), c_int32, c_void_p]
+                                          POINTER(c_int32), c_void_p, c_void_p, c_int32, c_void_p]
     return lib
 
 
@@ -215,9 +215,10 @@ def denoise_loop(dims, layout, blocks, n_intervals, sigmas_video, sigmas_audio, 
 
 def dit_attention_forward(q, k, v, o, batch, seq_pad, heads, head_dim, batch_stride, row_stride,
                           o_batch_stride, o_row_stride, valid_lens, attn_mode=DIT_ATTN_VALID_ONLY,
-                          stream=None):
+                          stream=None, q_gain=None, k_gain=None):
     vl = (c_int32 * len(valid_lens))(*[int(x) for x in valid_lens])
     _check(lib.dit_attention_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, seq_pad, heads,
                                      head_dim, batch_stride, row_stride, o_batch_stride,
-                                     o_row_stride, vl, attn_mode, _stream(stream)),
+                                     o_row_stride, vl, _ptr(q_gain), _ptr(k_gain), attn_mode,
+                                     _stream(stream)),
            "dit_attention_forward")

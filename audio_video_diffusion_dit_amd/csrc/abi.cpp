@@ -193,6 +193,7 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
   at.fixed_valid = attn_mode == DIT_ATTN_FIXED_VALID ? 1 : 0;
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
   at.valid[0] = rows.n_valid;
+  at.q_gain = w->q_g; at.k_gain = w->k_g;  // q, k come out of the Q/K RMSNorm with these gains
   if ((st = device_status(launch_attention(at, s), "attention")) != DIT_OK) return st;
 
   GemmArgs go{};
@@ -399,10 +400,12 @@ int denoise_loop(const dit_dims* dims, const dit_layout* layout,
 int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                           int32_t batch, int32_t seq_pad, int32_t heads, int32_t head_dim,
                           int64_t batch_stride, int64_t row_stride, int64_t o_batch_stride,
-                          int64_t o_row_stride, const int32_t* valid_lens, int32_t attn_mode,
-                          void* stream) {
+                          int64_t o_row_stride, const int32_t* valid_lens, const float* q_gain,
+                          const float* k_gain, int32_t attn_mode, void* stream) {
   g_err.clear();
   if (!q || !k || !v || !o || !valid_lens) return fail(DIT_ERR_INVALID, "null pointer argument");
+  if ((q_gain == nullptr) != (k_gain == nullptr))
+    return fail(DIT_ERR_INVALID, "q_gain and k_gain must both be given or both be NULL");
   if (batch < 1 || batch > avdit::ATTN_MAX_BATCH)
     return fail(DIT_ERR_INVALID, "batch %d outside [1, %d]", batch, (int)avdit::ATTN_MAX_BATCH);
   if (seq_pad < 0 || seq_pad > kMaxSeq) return fail(DIT_ERR_INVALID, "seq_pad %d out of range", seq_pad);
@@ -433,6 +436,7 @@ int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* 
   a.batch = batch; a.seq_pad = seq_pad; a.heads = heads; a.head_dim = head_dim;
   a.fixed_valid = attn_mode == DIT_ATTN_FIXED_VALID ? 1 : 0;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  a.q_gain = q_gain; a.k_gain = k_gain;
   (void)hipGetLastError();
   return device_status(avdit::launch_attention(a, static_cast<hipStream_t>(stream)), "attention");
 }

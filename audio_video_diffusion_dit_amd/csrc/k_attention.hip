@@ -21,8 +21,15 @@
 //    tile, and the next tile's loads are in flight during the current tile's math. The key
 //    loop is unrolled by two so that both LDS buffers are addressed with immediate offsets.
 //  * Only the last partial tile (and, in fixed-valid mode, the tiles past the valid length)
-//    run the masking code, and the accumulator rescale runs only on tiles where some row's
-//    maximum grew.
+//    run the masking code.
+//  * Softmax shift: q and k of the DiT block come out of the per-head Q/K RMSNorm, so every
+//    logit is bounded by max|gq| max|gk| sqrt(Dh) (a normalised head vector has norm below
+//    sqrt(Dh)). When the caller passes the gains and that bound, in log2 units, is at most 60,
+//    the bound replaces the running row maximum: probabilities stay in [2^-120, 1], the
+//    per-tile max reduction, cross-lane exchange and rescale disappear, and the row sum is
+//    taken from the bf16 probabilities the P V product uses (v_dot2c_f32_bf16). Otherwise the
+//    exact running maximum is kept, with the accumulator rescale run only on tiles where some
+//    row's maximum grew.
 //  * Valid-only mode bounds the key sweep by the request's valid length and query tiles that
 //    lie wholly in the tail only write zeros. Fixed-valid mode sweeps the whole padded
 //    length with a key mask. A fully masked tile leaves the running max, the sum and the
@@ -228,11 +235,34 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   float l_run = 0.0f;
   const float c = a.scale_log2;
 
+  // Logit bound from the Q/K RMSNorm gains: a normalised head vector has norm below sqrt(Dh),
+  // so |q.k| < max|gq| max|gk| Dh; the factor 1 + 2^-6 covers the bf16 rounding of q and k.
+  // In log2 units (times c) a bound up to 60 keeps every probability exp2(s c - bound) within
+  // [2^-120, 1], normal in fp32 and bf16: the bound then serves as the row maximum.
+  float bound = INFINITY;
+  if (a.q_gain != nullptr && a.k_gain != nullptr) {
+    float gq = 0.0f, gk = 0.0f;
+    for (int i = lane; i < DH; i += 64) {
+      gq = fmaxf(gq, fabsf(a.q_gain[i]));
+      gk = fmaxf(gk, fabsf(a.k_gain[i]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      gq = fmaxf(gq, __shfl_xor(gq, o, 64));
+      gk = fmaxf(gk, __shfl_xor(gk, o, 64));
+    }
+    bound = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+        int, gq * gk * (float)DH * c * (1.0f + 1.0f / 64.0f))));
+  }
+  const bool fixed_max = bound <= 60.0f;  // false for an infinite or NaN bound
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+
   const int key_end = a.fixed_valid ? L : V;
   const int nkt = (key_end + kKB - 1) / kKB;
   const int n_full = V / kKB;  // tiles whose 64 keys are all valid
 
-  auto tile = [&](auto masked_c, auto buf_c, int kt) {
+  auto tile = [&](auto fixed_c, auto masked_c, auto buf_c, int kt) __attribute__((always_inline)) {
+    constexpr bool FIXED = decltype(fixed_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr int BUF = decltype(buf_c)::value;
     const bool more = kt + 1 < nkt;
@@ -263,27 +293,32 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         }
     }
 
-    // ---- online softmax in base 2 with the scale folded into c ----
-    float mx = sacc[0][0];
+    // ---- softmax in base 2 with the scale folded into c ----
+    float mc;
+    if (FIXED) {
+      mc = bound;
+    } else {
+      // Online: the running max is exact (the largest probability of a row is exactly 1).
+      // The accumulator rescale is skipped when no lane's max grew: alpha would be exactly 1.
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
-    mx = pair_max(mx);
-    // The running max is exact (the largest probability of a row is exactly 1). The
-    // accumulator rescale is skipped when no lane's max grew: alpha would be exactly 1.
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = m_new > m_run;  // false for a fully masked tile (mx = -inf)
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-      m_run = m_new;
-      l_run *= alpha;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[h2][e]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = m_new > m_run;  // false for a fully masked tile (mx = -inf)
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+          for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+      }
+      mc = (m_run == -INFINITY) ? 0.0f : m_run * c;
     }
-    const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c;
     float psum = 0.0f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -291,9 +326,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][e], c, -mc));
         sacc[h2][e] = p;
-        psum += p;
+        if (!FIXED) psum += p;
       }
-    l_run += psum;
+    if (!FIXED) l_run += psum;
 
     // ---- O^T += V^T P^T, 4 k-steps of 16 keys ----
 #pragma unroll
@@ -305,6 +340,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       const uint32_t p2 = pack_bf16x2(sacc[h2][4 * j0 + 4], sacc[h2][4 * j0 + 5]);
       const uint32_t p3 = pack_bf16x2(sacc[h2][4 * j0 + 6], sacc[h2][4 * j0 + 7]);
       const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{p0, p1, p2, p3});
+      if (FIXED) {
+        // row sum of the probabilities exactly as rounded for the P V product
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p0), ones2, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p1), ones2, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p2), ones2, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p3), ones2, l_run, false);
+      }
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         lds_char* base = lds + BUF * BUFB + vaddr[t] + (16 * ps) * NC * 16;
@@ -320,20 +362,26 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     __syncthreads();
   };
 
+  auto sweep = [&](auto fixed_c) __attribute__((always_inline)) {
+    int kt = 0;
+    for (; kt + 2 <= n_full; kt += 2) {
+      tile(fixed_c, std::false_type{}, std::integral_constant<int, 0>{}, kt);
+      tile(fixed_c, std::false_type{}, std::integral_constant<int, 1>{}, kt + 1);
+    }
+    for (; kt < nkt; ++kt) {
+      if (kt & 1)
+        tile(fixed_c, std::true_type{}, std::integral_constant<int, 1>{}, kt);
+      else
+        tile(fixed_c, std::true_type{}, std::integral_constant<int, 0>{}, kt);
+    }
+  };
   load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= n_full; kt += 2) {
-    tile(std::false_type{}, std::integral_constant<int, 0>{}, kt);
-    tile(std::false_type{}, std::integral_constant<int, 1>{}, kt + 1);
-  }
-  for (; kt < nkt; ++kt) {
-    if (kt & 1)
-      tile(std::true_type{}, std::integral_constant<int, 1>{}, kt);
-    else
-      tile(std::true_type{}, std::integral_constant<int, 0>{}, kt);
-  }
+  if (fixed_max)
+    sweep(std::true_type{});
+  else
+    sweep(std::false_type{});
 
   // ---- normalise and store: element (j, i) of oacc[t] is d = 32 t + 8 j + 4 hh + i ----
   const float l_tot = pair_sum(l_run);

@@ -92,6 +92,11 @@ struct AttnArgs {
   int32_t batch, seq_pad, heads, head_dim;
   int32_t fixed_valid;  // 1: sweep the whole padded length with a key mask
   float scale_log2;     // log2(e) / sqrt(head_dim)
+  // Optional per-dimension gains [head_dim] of the Q/K RMSNorm that produced q and k (both or
+  // neither). With them the kernel bounds every logit and, when the bound is small enough,
+  // replaces the running row maximum by that bound (softmax is shift invariant).
+  const float* q_gain;
+  const float* k_gain;
   int32_t valid[ATTN_MAX_BATCH];
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -183,7 +183,8 @@ def main():
 
     def attn():
         N.dit_attention_forward(qkv, qkv + 2 * D, qkv + 4 * D, att, 1, L, H, Dh, L * 3 * D, 3 * D,
-                                L * D, D, [wl.n_valid], N.DIT_ATTN_VALID_ONLY, stream=stream)
+                                L * D, D, [wl.n_valid], N.DIT_ATTN_VALID_ONLY, stream=stream,
+                                q_gain=bw[0].q_g, k_gain=bw[0].k_g)
 
     attn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

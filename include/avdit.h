@@ -186,12 +186,18 @@ int denoise_loop(const dit_dims* dims, const dit_layout* layout,
  * (b, i, h, d) is at ptr[b * batch_stride + i * row_stride + h * head_dim + d] (strides in
  * elements, row_stride a multiple of 8; q, k, v share strides, o has its own). For the
  * block's qkv buffer, q = qkv, k = qkv + D, v = qkv + 2D with row_stride 3D.
- * valid_lens: host int32 [batch], each in [0, seq_pad]; batch <= 64; head_dim 64 or 128. */
+ * valid_lens: host int32 [batch], each in [0, seq_pad]; batch <= 64; head_dim 64 or 128.
+ * q_gain, k_gain: dev fp32 [head_dim] or both NULL. When given, q and k must be outputs of the
+ * per-head Q/K RMSNorm with these gains ([P3] "Changes Made": fused Q/K RMSNorm), which bounds
+ * every logit by max|q_gain| max|k_gain| sqrt(head_dim); the kernel then may use that bound in
+ * place of the running row maximum (same result up to rounding). Passing gains for q, k that
+ * did not come out of such a norm is undefined. */
 int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           uint16_t* o, int32_t batch, int32_t seq_pad, int32_t heads,
                           int32_t head_dim, int64_t batch_stride, int64_t row_stride,
                           int64_t o_batch_stride, int64_t o_row_stride,
-                          const int32_t* valid_lens, int32_t attn_mode, void* stream);
+                          const int32_t* valid_lens, const float* q_gain, const float* k_gain,
+                          int32_t attn_mode, void* stream);
 
 #ifdef __cplusplus
 }

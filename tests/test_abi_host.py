@@ -141,14 +141,17 @@ def test_entry_points_reject_invalid_arguments_without_device_work(N):
     # attention: head_dim, batch, valid length, strides
     vl = (N.c_int32 * 2)(10, 700)
     assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 2, 640, 4, 64, 640 * 256,
-                                       256, 640 * 256, 256, vl, 0, None) == N.DIT_ERR_INVALID
+                                       256, 640 * 256, 256, vl, None, None, 0, None) == N.DIT_ERR_INVALID
     vl = (N.c_int32 * 1)(10)
     assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1, 640, 4, 96, 0,
-                                       384, 0, 384, vl, 0, None) == N.DIT_ERR_UNSUPPORTED
+                                       384, 0, 384, vl, None, None, 0, None) == N.DIT_ERR_UNSUPPORTED
     assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 0, 640, 4, 64, 0,
-                                       256, 0, 256, vl, 0, None) == N.DIT_ERR_INVALID
+                                       256, 0, 256, vl, None, None, 0, None) == N.DIT_ERR_INVALID
     assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1, 640, 4, 64, 0,
-                                       200, 0, 256, vl, 0, None) == N.DIT_ERR_INVALID
+                                       200, 0, 256, vl, None, None, 0, None) == N.DIT_ERR_INVALID
+    # gains: both or neither
+    assert N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1, 640, 4, 64, 0,
+                                       256, 0, 256, vl, 1 << 24, None, 0, None) == N.DIT_ERR_INVALID
 
 
 def test_denoise_loop_rejects_invalid_arguments(N):

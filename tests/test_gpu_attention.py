@@ -17,16 +17,17 @@ def N():
     return _native
 
 
-def _run(N, q, k, v, valid, mode, o_fill=None):
+def _run(N, q, k, v, valid, mode, o_fill=None, gains=None):
     import torch
-    from audio_video_diffusion_dit_amd.device import to_dev_bf16, bf16_bits_of
+    from audio_video_diffusion_dit_amd.device import to_dev_bf16, to_dev_f32, bf16_bits_of
     B, L, H, Dh = q.shape
     dq, dk, dv = (to_dev_bf16(t) for t in (q, k, v))
     do = torch.empty((B, L, H, Dh), dtype=torch.bfloat16, device="cuda")
     if o_fill is not None:
         do.view(torch.int16).fill_(o_fill)
+    gq, gk = (None, None) if gains is None else (to_dev_f32(gains[0]), to_dev_f32(gains[1]))
     N.dit_attention_forward(dq, dk, dv, do, B, L, H, Dh, L * H * Dh, H * Dh, L * H * Dh, H * Dh,
-                            valid, mode)
+                            valid, mode, q_gain=gq, k_gain=gk)
     torch.cuda.synchronize()
     return bf16_bits_of(do)
 
@@ -120,3 +121,40 @@ def test_attention_ragged_batch_full_size(N):
         rows = np.sort(np.concatenate([rng.choice(n, 22, replace=False), [0, n - 1]]))
         ref = O.attention_rows(bf16_to_f32(q[b, rows]), bf16_to_f32(k[b]), bf16_to_f32(v[b]), n)
         assert_close(bf16_to_f32(vo[b, rows]), ref, f"request {b} (valid {n}), sampled rows")
+
+
+@pytest.mark.parametrize("head_dim,gain", [(64, 1.0), (128, 1.0), (128, 1.9), (128, 6.0)])
+def test_attention_with_qk_norm_gains(N, head_dim, gain):
+    """q and k that came out of the per-head Q/K RMSNorm with gains gq, gk have logits bounded by
+    max|gq| max|gk| sqrt(Dh). Given the gains, the kernel uses that bound in place of the running
+    row maximum when it is small enough (gain 1 and 1.9) and keeps the online maximum otherwise
+    (gain 6). Every case matches the oracle; fixed-valid and valid-only still agree bit for bit,
+    and garbage in the tail rows still leaves the outputs bitwise unchanged."""
+    import oracle as O
+    from audio_video_diffusion_dit_amd.inputs import attention_case, bf16_bits, bf16_to_f32
+    valid = (1, 77, 300, 513)
+    L, H = 520, 3
+    say(f"attention with Q/K norm gains: L={L} H={H} Dh={head_dim} gain={gain} valid={valid}")
+    q, k, v = attention_case(len(valid), L, H, head_dim, valid, seed=5)
+    ramp = np.linspace(0.3, 1.0, head_dim)
+    gq = (gain * ramp * np.where(np.arange(head_dim) % 4 == 1, -1.0, 1.0)).astype(np.float32)
+    gk = (gain * ramp[::-1]).astype(np.float32)
+
+    def qk_norm(t, g):
+        x = bf16_to_f32(t).astype(np.float64)
+        y = O.qk_rms_norm(x.reshape(-1, H, head_dim), g.astype(np.float64), 1e-6).reshape(x.shape)
+        return bf16_bits(y.astype(np.float32))
+
+    qn, kn = qk_norm(q, gq), qk_norm(k, gk)
+    ref = _oracle(qn, kn, v, valid)
+    got = _run(N, qn, kn, v, valid, N.DIT_ATTN_VALID_ONLY, o_fill=0x7FC0, gains=(gq, gk))
+    got_fv = _run(N, qn, kn, v, valid, N.DIT_ATTN_FIXED_VALID, o_fill=0x7FC0, gains=(gq, gk))
+    assert np.array_equal(got, got_fv), "fixed-valid and valid-only must agree bit for bit"
+    qg, kg, vg = qn.copy(), kn.copy(), v.copy()
+    for b, n in enumerate(valid):
+        qg[b, n:], kg[b, n:], vg[b, n:] = 0x7FC0, 0xFF80, 0x7F80  # NaN, -inf, +inf in the tail
+    got_g = _run(N, qg, kg, vg, valid, N.DIT_ATTN_VALID_ONLY, gains=(gq, gk))
+    assert np.array_equal(got, got_g), "tail contents must not change the outputs"
+    for b, n in enumerate(valid):
+        assert np.all(got[b, n:] == 0)
+        assert_close(bf16_to_f32(got[b, :n]), ref[b, :n], f"req {b} (valid {n}, gain {gain})")

@@ -168,3 +168,41 @@ def test_block_h3_sampled_rows(env):
     ref = O.block_forward(x_values(case.x), oracle_block(case.blocks[0]), case.temb,
                           oracle_dims(wl), oracle_layout(wl), rows=rows)
     assert_close(got[rows], ref, "block_h3 sampled rows")
+
+
+@pytest.mark.parametrize("name,gain,path", [("block_small", -2.0, "bound"),
+                                            ("block_small", 3.0, "online"),
+                                            ("block_odd", 1.8, "bound"),
+                                            ("block_odd", 4.0, "online")])
+def test_block_attention_softmax_paths(env, name, gain, path):
+    """The Q/K RMSNorm gains bound every attention logit by max|gq| max|gk| sqrt(Dh); when that
+    bound (in log2 units, with a 1 + 2^-6 margin) is at most 60 the kernel uses it in place of the
+    running row maximum, otherwise it keeps the online maximum. Both paths match the oracle, per
+    kernel and end to end, with gains that vary across the head dimension and change sign."""
+    import oracle as O
+    N, dev = env
+    case = _case(name, seed=3)
+    wl = case.wl
+    V, D, H, Dh = wl.n_valid, wl.hidden, wl.heads, wl.head_dim
+    ramp = np.linspace(0.25, 1.0, Dh, dtype=np.float32)
+    sign = np.where(np.arange(Dh) % 3 == 0, -1.0, 1.0).astype(np.float32)
+    blk_p = dataclasses.replace(case.blocks[0], q_g=(gain * ramp * sign).astype(np.float32),
+                                k_g=(gain * ramp[::-1] * sign).astype(np.float32))
+    case = dataclasses.replace(case, blocks=[blk_p])
+    bound = gain * gain * Dh * (np.log2(np.e) / np.sqrt(Dh)) * (1 + 2 ** -6)
+    assert (bound <= 60) == (path == "bound"), bound
+    say(f"block {name}: gains up to |{gain}|, logit bound {bound:.1f} (log2 units) -> {path} path")
+    out, ws, m = _gpu_block(env, case)
+    got = dev.bf16_values_of(out).astype(np.float64)
+    blk = oracle_block(blk_p)
+    dims, lay = oracle_dims(wl), oracle_layout(wl)
+    ref = O.block_forward(x_values(case.x), blk, case.temb, dims, lay)
+    assert np.all(got[V:] == 0)
+    assert_close(got[:V], ref[:V], f"{name} block output ({path} softmax path)")
+    it = _inter(dev, ws, m, wl)
+    q_g = it["qkv"][:V, :D].reshape(V, H, Dh)
+    k_g = it["qkv"][:V, D:2 * D].reshape(V, H, Dh)
+    v_g = it["qkv"][:V, 2 * D:].reshape(V, H, Dh)
+    o_ref = O.attention_valid(q_g, k_g, v_g, V).reshape(V, D)
+    assert_kernel_close(it["o"][:V], o_ref, f"attention ({path} softmax path)")
+    assert np.all(it["o"][V:] == 0)
