@@ -121,8 +121,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int hh = lane >> 5;
   const int wave = tid >> 6;
   // Workgroup ids are dealt round-robin over the 8 XCDs; remap them so that each XCD receives a
-  // contiguous range of (request, head, query-tile) triples, query tile fastest: the query
-  // tiles of one head then run on one XCD and share its K/V tiles in that XCD's L2.
+  // contiguous range of (head, request, query-tile) triples, query tile fastest: the query
+  // tiles of one (request, head) then run on one XCD and share its K/V tiles in that XCD's L2,
+  // and with the request varying faster than the head each XCD's range mixes the requests of a
+  // ragged batch, so short and long requests spread evenly over the XCDs.
   const int n_qt = gridDim.x;
   const int total = gridDim.x * gridDim.y * gridDim.z;
   const int b_lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -130,8 +132,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int per = total >> 3, rem = total & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
   const int qt = logical % n_qt;
-  const int head = (logical / n_qt) % gridDim.y;
-  const int bq = logical / (n_qt * gridDim.y);
+  const int pair = logical / n_qt;
+  const int bq = pair % gridDim.z;
+  const int head = pair / gridDim.z;
   const int q0 = qt * kQB;
   const int V = a.valid[bq];
   const int L = a.seq_pad;

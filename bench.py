@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-off", action="store_true", help="skip the cache-off loop")
     p.add_argument("--roofline-only", action="store_true",
                    help="one block, the attention timing and the counter-calibration copy only")
+    p.add_argument("--configs", action="store_true",
+                   help="per-workload report instead of the bench line: GPU and float64-oracle "
+                        "timings of every configuration, one JSON line each")
     return p.parse_args()
 
 
@@ -104,12 +107,180 @@ def cpu_baseline(case, rows_n):
                       f"{rows_n} sampled output rows; {flops:.3e} useful FLOPs"}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
+def configs_report(args):
+    """GPU and float64-oracle timings of every workload, one JSON line per measurement.
+
+    GPU: 3 warm-up calls, then the median of 10 single-call timings with HIP events on the
+    stream (loops: median of 3). Useful FLOPs count valid tokens only (8VD^2 + 6VDF + 4V^2D per
+    block; attention 4 v^2 H Dh per request). Oracle: the float64 NumPy implementation on the
+    host cores, on the whole block where that takes seconds, else on a sample of output rows
+    (keys and values for every valid row), in the same useful-FLOP unit; the 4-block loop's
+    oracle time is extrapolated from one full block and labelled so.
+    """
+    import statistics
+    import numpy as np
+    import torch
+    import oracle as O
+    from audio_video_diffusion_dit_amd import _native as N
+    from audio_video_diffusion_dit_amd import device as dev
+    from audio_video_diffusion_dit_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    meta = {"device": props.name, "cus": props.multi_processor_count, "hip": torch.version.hip,
+            "oracle_threads": int(_blas_threads()), "host_cores": len(os.sched_getaffinity(0))}
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def gpu_ms(fn, warm=3, reps=10):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    def emit(rec):
+        rec["meta"] = meta
+        print(json.dumps(rec), flush=True)
+
+    def block_flops(V, D, F):
+        return 8.0 * V * D * D + 6.0 * V * D * F + 4.0 * float(V) ** 2 * D
+
+    def oracle_block(case, rows_n):
+        wl = case.wl
+        V, D, F = wl.n_valid, wl.hidden, wl.ffn
+        blk = {k: np.asarray(v, dtype=np.float64) for k, v in case.blocks[0].as_float().items()}
+        x = I.bf16_to_f32(case.x).astype(np.float64)
+        dims = O.Dims(D, wl.heads, wl.head_dim, F)
+        lay = O.Layout(wl.n_video, wl.n_audio, wl.seq_pad)
+        if rows_n is None or rows_n >= V:
+            t0 = time.perf_counter()
+            O.block_forward(x, blk, case.temb, dims, lay)
+            dt = time.perf_counter() - t0
+            return {"seconds": round(dt, 3), "value": block_flops(V, D, F) / dt / 1e12,
+                    "unit": "TFLOP/s", "sample": "whole block"}
+        rows = np.sort(np.random.default_rng(0).choice(V, rows_n, replace=False))
+        t0 = time.perf_counter()
+        O.block_forward(x, blk, case.temb, dims, lay, rows=rows)
+        dt = time.perf_counter() - t0
+        fl = 4.0 * V * D * D + rows_n * (4.0 * D * D + 6.0 * D * F + 4.0 * V * D)
+        return {"seconds": round(dt, 3), "value": fl / dt / 1e12, "unit": "TFLOP/s",
+                "sample": f"{rows_n} sampled output rows, keys/values for all {V} rows"}
+
+    # ---- single blocks: the 640-token block, the H3-scale block, one block of each loop ----
+    for name, rows_n in (("block_small", None), ("loop_4blk", None), ("block_h3", 256),
+                         ("loop_8blk_32k", 256)):
+        wl = I.WORKLOADS[name]
+        log(f"[configs] block {name}")
+        case = I.block_case(wl, seed=0, n_blocks=1)
+        dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+        blk = dev.upload_block(case.blocks[0])
+        x = dev.to_dev_bf16(case.x)
+        temb = dev.to_dev_f32(case.temb)
+        out = torch.empty_like(x)
+        ws, _ = dev.workspace(dims, lay, 0)
+        ms = gpu_ms(lambda: N.dit_block_forward(dims, lay, blk.weights, temb, x, out,
+                                                N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
+        fl = block_flops(wl.n_valid, wl.hidden, wl.ffn)
+        orc = oracle_block(case, rows_n)
+        emit({"workload": name, "kind": "block", "valid": wl.n_valid, "seq_pad": wl.seq_pad,
+              "hidden": wl.hidden, "ffn": wl.ffn, "heads": wl.heads, "head_dim": wl.head_dim,
+              "useful_flops": fl, "gpu_ms": round(ms, 4), "gpu_tflops": round(fl / ms / 1e9, 2),
+              "frac_of_2.5PF": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+              "oracle": {**orc, "value": round(orc["value"], 5)},
+              "oracle_full_block_s_est": round(fl / (orc["value"] * 1e12), 2)})
+        del ws, blk, x, out
+
+    # ---- the 4-block 49-interval loop, cache off and conservative ----
+    wl = I.WORKLOADS["loop_4blk"]
+    log("[configs] loop loop_4blk")
+    case = I.loop_case(wl, seed=0)
+    dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+    blocks = dev.upload_blocks(case.blocks)
+    bw = [b.weights for b in blocks]
+    temb = dev.to_dev_f32(case.temb_steps)
+    x0 = dev.to_dev_f32(case.x0)
+    x = torch.empty_like(x0)
+    ws, _ = dev.workspace(dims, lay, len(blocks))
+    res = {}
+    for mode in ("off", "conservative"):
+        pol = N.make_policy(mode)
+        stats = {}
+
+        def run():
+            x.copy_(x0)
+            stats["s"] = N.denoise_loop(dims, lay, bw, wl.n_intervals, case.sigmas_video,
+                                        case.sigmas_audio, temb, pol, x, N.DIT_ATTN_VALID_ONLY,
+                                        ws, stream=stream, want_hits=False)[0]
+        ms = gpu_ms(run, warm=1, reps=3)
+        st = stats["s"]
+        res[mode] = {"ms_per_loop": round(ms, 3), "steps_per_sec": round(wl.n_intervals / ms * 1e3, 2),
+                     "useful_tflops": round(st.useful_flops / ms / 1e9, 2),
+                     "dit_calls": st.dit_calls, "cache_hits": st.cache_hits}
+    one = I.block_case(wl, seed=0, n_blocks=1)
+    orc = oracle_block(one, None)
+    t_blk = orc["seconds"]
+    ext = {m: round(r["dit_calls"] * wl.n_blocks * t_blk, 1) for m, r in res.items()}
+    emit({"workload": wl.name, "kind": "loop", "intervals": wl.n_intervals, "blocks": wl.n_blocks,
+          "valid": wl.n_valid, "gpu": res,
+          "oracle": {"one_block_seconds": t_blk, "loop_seconds_extrapolated": ext,
+                     "note": "extrapolated: dit_calls x blocks x one float64 block (Euler steps negligible)"}})
+    del ws, blocks, x, x0
+
+    # ---- ragged valid-only attention: 4 requests of 8192 rows, 16 heads x 128 ----
+    log("[configs] attention ragged")
+    B, L, H, Dh = 4, 8192, 16, 128
+    valid = (3000, 5100, 7777, 8192)
+    q, k, v = I.attention_case(B, L, H, Dh, valid, seed=7)
+    dq, dk, dv = (dev.to_dev_bf16(t) for t in (q, k, v))
+    do = torch.empty((B, L, H, Dh), dtype=torch.bfloat16, device="cuda")
+    useful = sum(4.0 * n * n * H * Dh for n in valid)
+    launched = 4.0 * B * L * L * H * Dh
+    out = {}
+    for mode, name in ((N.DIT_ATTN_VALID_ONLY, "valid_only"), (N.DIT_ATTN_FIXED_VALID, "fixed_valid")):
+        ms = gpu_ms(lambda: N.dit_attention_forward(dq, dk, dv, do, B, L, H, Dh, L * H * Dh, H * Dh,
+                                                    L * H * Dh, H * Dh, valid, mode, stream=stream))
+        out[name] = {"ms": round(ms, 4), "useful_tflops": round(useful / ms / 1e9, 2)}
+    rows_per = 64
+    dt = 0.0
+    for b, n in enumerate(valid):
+        rows = np.sort(np.random.default_rng(b).choice(n, rows_per, replace=False))
+        qb, kb, vb = (I.bf16_to_f32(t[b, :n]).astype(np.float64) for t in (q, k, v))
+        t0 = time.perf_counter()
+        O.attention_rows(qb[rows], kb, vb, n)
+        dt += time.perf_counter() - t0
+    fl = sum(4.0 * rows_per * n * H * Dh for n in valid)
+    emit({"workload": "attn_ragged", "kind": "attention", "batch": B, "seq_pad": L, "heads": H,
+          "head_dim": Dh, "valid": list(valid), "useful_flops": useful,
+          "fixed_valid_launched_flops": launched, "useful_over_launched": round(useful / launched, 4),
+          "gpu": out, "oracle": {"seconds": round(dt, 3), "value": round(fl / dt / 1e12, 5),
+                                 "unit": "TFLOP/s",
+                                 "sample": f"{rows_per} query rows per request, all heads and keys"}})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+
+    if args.configs:
+        configs_report(args)
+        return
 
     import numpy as np
     import torch
