@@ -52,6 +52,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kQB = 128;                    // queries per workgroup
 constexpr int kKB = 64;                     // keys per tile
+constexpr int kKPF = 4;                     // K fragments read ahead in the score phase
 constexpr int32_t kAttnRsrcWord3 = 0x00020000;
 
 // 16-byte-chunk XOR swizzle of a K row: 16 consecutive rows read at one logical chunk hit
@@ -273,16 +274,36 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
     // ---- S^T = K Q^T for 64 keys x 32 queries ----
     f32x16 sacc[2];
+    {
+      // K fragments are read kKPF MFMAs ahead of their use through a ring of registers, and the
+      // issue order is pinned (left alone, the scheduler moves each read next to its MFMA and
+      // the LDS latency lands in front of every MFMA of the first chain)
+      constexpr int NS = 2 * QS;
+      bf16x8 kr[kKPF];
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+                                              lds + BUF * BUFB + kaddr_of(i / QS, i % QS)));
+      };
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+      for (int i = 0; i < kKPF; ++i) kr[i] = kread(i);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lds + BUF * BUFB + kaddr_of(h2, s)));
-        sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[h2], 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        sacc[0][e] = 0.0f;
+        sacc[1][e] = 0.0f;
       }
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const bf16x8 kf = kr[i % kKPF];
+        if (i + kKPF < NS) kr[i % kKPF] = kread(i + kKPF);
+        sacc[i / QS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i % QS], sacc[i / QS], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kKPF, 0);  // kKPF LDS reads
+#pragma unroll
+      for (int i = 0; i + kKPF < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kKPF, 0);  // the last kKPF MFMAs
     }
     // element (j, i) of sacc[h2] is key kt * 64 + 32 h2 + 8 j + 4 hh + i
     if (MASKED) {
