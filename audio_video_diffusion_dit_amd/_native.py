@@ -21,7 +21,8 @@ DIT_ATTN_VALID_ONLY, DIT_ATTN_FIXED_VALID = 0, 1
 DIT_CACHE_OFF, DIT_CACHE_VELOCITY = 0, 1
 
 EXPORTED = ("dit_last_error", "dit_version", "dit_cache_schedule", "dit_workspace_size",
-            "dit_block_forward", "step_update", "denoise_loop", "dit_attention_forward")
+            "dit_block_forward", "dit_block_forward_f32", "step_update", "denoise_loop",
+            "denoise_loop_f32", "dit_attention_forward")
 
 
 class DitDims(ctypes.Structure):
@@ -81,6 +82,8 @@ def _load():
     lib.dit_block_forward.argtypes = [POINTER(DitDims), POINTER(DitLayout), POINTER(DitBlockWeights),
                                       c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                       c_void_p]
+    lib.dit_block_forward_f32.restype = c_int32
+    lib.dit_block_forward_f32.argtypes = lib.dit_block_forward.argtypes
     lib.step_update.restype = c_int32
     lib.step_update.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(DitLayout), c_int32, c_float,
                                 c_float, c_void_p]
@@ -89,6 +92,8 @@ def _load():
                                  c_int32, c_int32, POINTER(c_float), POINTER(c_float), c_void_p,
                                  POINTER(DitCachePolicy), c_void_p, c_int32, POINTER(DitLoopStats),
                                  c_void_p, c_size_t, c_void_p]
+    lib.denoise_loop_f32.restype = c_int32
+    lib.denoise_loop_f32.argtypes = lib.denoise_loop.argtypes
     lib.dit_attention_forward.restype = c_int32
     lib.dit_attention_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                           c_int32, c_int32, c_int64, c_int64, c_int64, c_int64,
@@ -179,11 +184,21 @@ def dit_workspace_size(dims: DitDims, layout: DitLayout, n_blocks: int = 0):
 
 def dit_block_forward(dims, layout, weights: DitBlockWeights, temb, x_in, x_out,
                       attn_mode=DIT_ATTN_VALID_ONLY, ws=None, ws_bytes=None, stream=None):
+    """x_in, x_out: bf16 [seq_pad, hidden] (fp32 for dit_block_forward_f32)."""
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     _check(lib.dit_block_forward(ctypes.byref(dims), ctypes.byref(layout), ctypes.byref(weights),
                                  _ptr(temb), _ptr(x_in), _ptr(x_out), attn_mode, _ptr(ws), ws_bytes,
                                  _stream(stream)), "dit_block_forward")
+
+
+def dit_block_forward_f32(dims, layout, weights: DitBlockWeights, temb, x_in, x_out,
+                          attn_mode=DIT_ATTN_VALID_ONLY, ws=None, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib.dit_block_forward_f32(ctypes.byref(dims), ctypes.byref(layout), ctypes.byref(weights),
+                                     _ptr(temb), _ptr(x_in), _ptr(x_out), attn_mode, _ptr(ws),
+                                     ws_bytes, _stream(stream)), "dit_block_forward_f32")
 
 
 def step_update(x, v, x_bf16, layout, hidden, dt_video, dt_audio, stream=None):
@@ -193,8 +208,9 @@ def step_update(x, v, x_bf16, layout, hidden, dt_video, dt_audio, stream=None):
 
 def denoise_loop(dims, layout, blocks, n_intervals, sigmas_video, sigmas_audio, temb_steps,
                  policy, x_latent, attn_mode=DIT_ATTN_VALID_ONLY, ws=None, ws_bytes=None,
-                 stream=None, want_hits=True):
+                 stream=None, want_hits=True, residual_f32=False):
     """blocks: list of DitBlockWeights; sigmas: host float sequences of length N + 1.
+    residual_f32 selects denoise_loop_f32 (fp32 residual stream).
     Returns the DitLoopStats and, with want_hits, the per-interval reuse flags."""
     arr = (DitBlockWeights * len(blocks))(*blocks)
     sv = (c_float * (n_intervals + 1))(*[float(s) for s in sigmas_video])
@@ -205,10 +221,11 @@ def denoise_loop(dims, layout, blocks, n_intervals, sigmas_video, sigmas_audio, 
         stats.step_hit = ctypes.cast(hit_buf, POINTER(c_uint8))
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
-    _check(lib.denoise_loop(ctypes.byref(dims), ctypes.byref(layout), arr, len(blocks), n_intervals,
-                            sv, sa, _ptr(temb_steps), ctypes.byref(policy), _ptr(x_latent),
-                            attn_mode, ctypes.byref(stats), _ptr(ws), ws_bytes, _stream(stream)),
-           "denoise_loop")
+    fn = lib.denoise_loop_f32 if residual_f32 else lib.denoise_loop
+    _check(fn(ctypes.byref(dims), ctypes.byref(layout), arr, len(blocks), n_intervals,
+              sv, sa, _ptr(temb_steps), ctypes.byref(policy), _ptr(x_latent),
+              attn_mode, ctypes.byref(stats), _ptr(ws), ws_bytes, _stream(stream)),
+           "denoise_loop_f32" if residual_f32 else "denoise_loop")
     hits = [bool(hit_buf[i]) for i in range(n_intervals)] if want_hits else None
     return stats, hits
 

@@ -125,10 +125,13 @@ void build_map(const dit_dims* d, const dit_layout* l, int32_t n_blocks, dit_wor
   m->ffn_ld = ffn_ld(d);
   m->act = off; off += align_up(L * (size_t)m->ffn_ld * 2);
   if (n_blocks >= 1) {
+    // ping, pong and velocity hold bf16 rows in the bf16-residual loop and fp32 rows in the
+    // fp32-residual loop: sized for fp32
+    const size_t row_f = align_up(L * D * 4);
     m->x_bf16 = off; off += row_d;
-    m->ping = off; off += row_d;
-    m->pong = off; off += row_d;
-    m->velocity = off; off += row_d;
+    m->ping = off; off += row_f;
+    m->pong = off; off += row_f;
+    m->velocity = off; off += row_f;
   } else {
     m->x_bf16 = m->ping = m->pong = m->velocity = 0;
   }
@@ -153,10 +156,12 @@ bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Enqueue one block on `s`: eight launches, no host synchronisation.
+// Enqueue one block on `s`: eight launches, no host synchronisation. x_in and x_out are bf16
+// rows, or fp32 rows when f32 (the fp32 residual stream: norm1 reads fp32, both gated
+// residual epilogues read and write fp32).
 int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weights* w,
-                  const float* temb, const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode,
-                  char* ws, const dit_workspace_map& m, hipStream_t s) {
+                  const float* temb, const void* x_in, void* x_out, int32_t attn_mode,
+                  char* ws, const dit_workspace_map& m, hipStream_t s, bool f32 = false) {
   using namespace avdit;
   const int32_t D = d->hidden, F = d->ffn, L = l->seq_pad;
   const RowLayout rows{l->n_video, l->n_video + l->n_audio, L};
@@ -171,6 +176,7 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
   NormModArgs n1{};
   n1.x = x_in; n1.h = h; n1.gain = w->norm1_g; n1.ada = w->ada; n1.temb = temb;
   n1.rows = rows; n1.D = D; n1.shift_chunk = 0; n1.scale_chunk = 1; n1.eps = d->norm_eps;
+  n1.x_f32 = f32 ? 1 : 0;
   if ((st = device_status(launch_norm_mod(n1, s), "norm1+modulation")) != DIT_OK) return st;
 
   GemmArgs g{};
@@ -198,7 +204,8 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
 
   GemmArgs go{};
   go.A = att; go.W = w->w_o; go.C = x1; go.lda = D; go.ldw = D; go.ldc = D; go.N = D; go.K = D;
-  go.rows = rows; go.epilogue = EPI_GATED_TO_F32; go.resid = x_in; go.ldr = D; go.ada = w->ada;
+  go.rows = rows; go.epilogue = f32 ? EPI_GATED_F32_TO_F32 : EPI_GATED_TO_F32; go.resid = x_in;
+  go.ldr = D; go.ada = w->ada;
   go.temb = temb; go.chunk = 2;
   if ((st = device_status(launch_gemm(go, s), "out projection")) != DIT_OK) return st;
 
@@ -215,7 +222,8 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
 
   GemmArgs gd{};
   gd.A = act; gd.W = w->w_down; gd.C = x_out; gd.lda = m.ffn_ld; gd.ldw = F; gd.ldc = D;
-  gd.N = D; gd.K = F; gd.rows = rows; gd.epilogue = EPI_GATED_F32_IN; gd.resid = x1; gd.ldr = D;
+  gd.N = D; gd.K = F; gd.rows = rows; gd.epilogue = f32 ? EPI_GATED_F32_TO_F32 : EPI_GATED_F32_IN;
+  gd.resid = x1; gd.ldr = D;
   gd.ada = w->ada; gd.temb = temb; gd.chunk = 5;
   if ((st = device_status(launch_gemm(gd, s), "down projection")) != DIT_OK) return st;
   return DIT_OK;
@@ -263,10 +271,14 @@ size_t dit_workspace_size(const dit_dims* dims, const dit_layout* layout, int32_
   return m.total;
 }
 
-int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
-                      const dit_block_weights* weights, const float* temb,
-                      const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int block_forward_impl(const dit_dims* dims, const dit_layout* layout,
+                       const dit_block_weights* weights, const float* temb, const void* x_in,
+                       void* x_out, int32_t attn_mode, void* ws, size_t ws_bytes, void* stream,
+                       bool f32) {
   g_err.clear();
   int st;
   if ((st = check_dims(dims)) != DIT_OK) return st;
@@ -275,10 +287,12 @@ int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
   if (!temb || !x_in || !x_out) return fail(DIT_ERR_INVALID, "temb, x_in and x_out must be non-null");
   if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
     return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
+  if (f32 && ((((uintptr_t)x_in) & 15) || (((uintptr_t)x_out) & 15)))
+    return fail(DIT_ERR_INVALID, "x_in and x_out must be 16-byte aligned");
   dit_workspace_map m;
   build_map(dims, layout, 0, &m);
   if ((st = check_ws(ws, ws_bytes, m.total)) != DIT_OK) return st;
-  const size_t act_bytes = (size_t)layout->seq_pad * dims->hidden * 2;
+  const size_t act_bytes = (size_t)layout->seq_pad * dims->hidden * (f32 ? 4 : 2);
   if (ranges_overlap(x_in, act_bytes, x_out, act_bytes) && act_bytes > 0)
     return fail(DIT_ERR_INVALID, "x_in and x_out overlap");
   if (act_bytes > 0 && (ranges_overlap(x_in, act_bytes, ws, m.total) ||
@@ -287,7 +301,27 @@ int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
   if (layout->seq_pad == 0) return DIT_OK;
   (void)hipGetLastError();
   return enqueue_block(dims, layout, weights, temb, x_in, x_out, attn_mode,
-                       static_cast<char*>(ws), m, static_cast<hipStream_t>(stream));
+                       static_cast<char*>(ws), m, static_cast<hipStream_t>(stream), f32);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
+                      const dit_block_weights* weights, const float* temb,
+                      const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return block_forward_impl(dims, layout, weights, temb, x_in, x_out, attn_mode, ws, ws_bytes,
+                            stream, false);
+}
+
+int dit_block_forward_f32(const dit_dims* dims, const dit_layout* layout,
+                          const dit_block_weights* weights, const float* temb, const float* x_in,
+                          float* x_out, int32_t attn_mode, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return block_forward_impl(dims, layout, weights, temb, x_in, x_out, attn_mode, ws, ws_bytes,
+                            stream, true);
 }
 
 int step_update(float* x, const uint16_t* v, uint16_t* x_bf16, const dit_layout* layout,
@@ -310,12 +344,15 @@ int step_update(float* x, const uint16_t* v, uint16_t* x_bf16, const dit_layout*
   return device_status(avdit::launch_step_update(a, static_cast<hipStream_t>(stream)), "step update");
 }
 
-int denoise_loop(const dit_dims* dims, const dit_layout* layout,
-                 const dit_block_weights* blocks, int32_t n_blocks, int32_t n_intervals,
-                 const float* sigmas_video, const float* sigmas_audio,
-                 const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
-                 int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_weights* blocks,
+              int32_t n_blocks, int32_t n_intervals, const float* sigmas_video,
+              const float* sigmas_audio, const float* temb_steps, const dit_cache_policy* policy,
+              float* x_latent, int32_t attn_mode, dit_loop_stats* stats, void* ws,
+              size_t ws_bytes, void* stream, bool f32) {
   g_err.clear();
   int st;
   if ((st = check_dims(dims)) != DIT_OK) return st;
@@ -353,14 +390,14 @@ int denoise_loop(const dit_dims* dims, const dit_layout* layout,
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);
     uint16_t* x_bf16 = reinterpret_cast<uint16_t*>(base + m.x_bf16);
-    uint16_t* vel = reinterpret_cast<uint16_t*>(base + m.velocity);
-    uint16_t* pp[2] = {reinterpret_cast<uint16_t*>(base + m.ping),
-                       reinterpret_cast<uint16_t*>(base + m.pong)};
+    void* vel = base + m.velocity;
+    void* pp[2] = {base + m.ping, base + m.pong};
     const avdit::RowLayout rows{layout->n_video, layout->n_video + layout->n_audio, layout->seq_pad};
     const size_t temb_step = (size_t)dims->n_mod * 6 * dims->hidden;
 
+    // zero the latent's tail rows; the bf16 loop also takes the bf16 copy of x_0 (its DiT input)
     avdit::StepArgs first{};
-    first.x = x_latent; first.v = nullptr; first.x_bf16 = x_bf16; first.rows = rows;
+    first.x = x_latent; first.x_bf16 = f32 ? nullptr : x_bf16; first.rows = rows;
     first.D = dims->hidden;
     if ((st = device_status(avdit::launch_step_update(first, s), "latent conversion")) != DIT_OK)
       return st;
@@ -368,15 +405,21 @@ int denoise_loop(const dit_dims* dims, const dit_layout* layout,
       if (!hits[i]) {
         const float* temb_i = temb_steps + (size_t)i * temb_step;
         for (int32_t b = 0; b < n_blocks; ++b) {
-          const uint16_t* in = b == 0 ? x_bf16 : pp[(b - 1) & 1];
-          uint16_t* out = b == n_blocks - 1 ? vel : pp[b & 1];
-          if ((st = enqueue_block(dims, layout, &blocks[b], temb_i, in, out, attn_mode, base, m, s)) !=
-              DIT_OK)
+          // the fp32 loop feeds the latent itself to the first block
+          const void* in = b > 0 ? pp[(b - 1) & 1] : (f32 ? (const void*)x_latent : (const void*)x_bf16);
+          void* out = b == n_blocks - 1 ? vel : pp[b & 1];
+          if ((st = enqueue_block(dims, layout, &blocks[b], temb_i, in, out, attn_mode, base, m, s,
+                                  f32)) != DIT_OK)
             return st;
         }
       }
       avdit::StepArgs a{};
-      a.x = x_latent; a.v = vel; a.x_bf16 = (i + 1 < n_intervals) ? x_bf16 : nullptr;
+      a.x = x_latent;
+      if (f32)
+        a.v_f32 = static_cast<const float*>(vel);
+      else
+        a.v = static_cast<const uint16_t*>(vel);
+      a.x_bf16 = (!f32 && i + 1 < n_intervals) ? x_bf16 : nullptr;
       a.rows = rows; a.D = dims->hidden;
       a.dt_video = sigmas_video[i + 1] - sigmas_video[i];
       a.dt_audio = sigmas_audio[i + 1] - sigmas_audio[i];
@@ -395,6 +438,30 @@ int denoise_loop(const dit_dims* dims, const dit_layout* layout,
     if (stats->step_hit && n_intervals > 0) std::memcpy(stats->step_hit, hits.data(), hits.size());
   }
   return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int denoise_loop(const dit_dims* dims, const dit_layout* layout,
+                 const dit_block_weights* blocks, int32_t n_blocks, int32_t n_intervals,
+                 const float* sigmas_video, const float* sigmas_audio,
+                 const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
+                 int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return loop_impl(dims, layout, blocks, n_blocks, n_intervals, sigmas_video, sigmas_audio,
+                   temb_steps, policy, x_latent, attn_mode, stats, ws, ws_bytes, stream, false);
+}
+
+int denoise_loop_f32(const dit_dims* dims, const dit_layout* layout,
+                     const dit_block_weights* blocks, int32_t n_blocks, int32_t n_intervals,
+                     const float* sigmas_video, const float* sigmas_audio,
+                     const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
+                     int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return loop_impl(dims, layout, blocks, n_blocks, n_intervals, sigmas_video, sigmas_audio,
+                   temb_steps, policy, x_latent, attn_mode, stats, ws, ws_bytes, stream, true);
 }
 
 int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,

@@ -286,7 +286,8 @@ hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s) {
 // and "Changes Made": independent video/audio schedulers, optimized scheduler updates).
 // One thread per 8 consecutive elements of a row and one pass over the grid (no grid-stride
 // loop), with non-temporal loads and stores: this streaming pattern measured 6.1-6.3 TB/s on
-// a plain copy against 4.7-4.9 TB/s for a grid-stride loop. The bf16 copy is the next DiT input.
+// a plain copy against 4.7-4.9 TB/s for a grid-stride loop. The bf16 copy is the next DiT input
+// of the bf16-residual loop; the fp32-residual loop takes an fp32 velocity and no copy.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_step_update(StepArgs a) {
   const int per_row = a.D >> 3;
@@ -304,18 +305,27 @@ __global__ __launch_bounds__(256) void k_step_update(StepArgs a) {
     return;
   }
   f32x4 x0 = __builtin_nontemporal_load(xp), x1 = __builtin_nontemporal_load(xp + 1);
-  if (a.v) {
+  if (a.v || a.v_f32) {
     const float dt = row < a.rows.n_video ? a.dt_video : a.dt_audio;
-    const u32x4 vv = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(a.v + (size_t)row * a.D + 8 * c));
-    x0.x = fmaf(dt, bf_lo(vv.x), x0.x);
-    x0.y = fmaf(dt, bf_hi(vv.x), x0.y);
-    x0.z = fmaf(dt, bf_lo(vv.y), x0.z);
-    x0.w = fmaf(dt, bf_hi(vv.y), x0.w);
-    x1.x = fmaf(dt, bf_lo(vv.z), x1.x);
-    x1.y = fmaf(dt, bf_hi(vv.z), x1.y);
-    x1.z = fmaf(dt, bf_lo(vv.w), x1.z);
-    x1.w = fmaf(dt, bf_hi(vv.w), x1.w);
+    f32x4 v0, v1;
+    if (a.v) {
+      const u32x4 vv = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(a.v + (size_t)row * a.D + 8 * c));
+      v0 = f32x4{bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y)};
+      v1 = f32x4{bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+    } else {
+      const f32x4* vp = reinterpret_cast<const f32x4*>(a.v_f32 + (size_t)row * a.D + 8 * c);
+      v0 = __builtin_nontemporal_load(vp);
+      v1 = __builtin_nontemporal_load(vp + 1);
+    }
+    x0.x = fmaf(dt, v0.x, x0.x);
+    x0.y = fmaf(dt, v0.y, x0.y);
+    x0.z = fmaf(dt, v0.z, x0.z);
+    x0.w = fmaf(dt, v0.w, x0.w);
+    x1.x = fmaf(dt, v1.x, x1.x);
+    x1.y = fmaf(dt, v1.y, x1.y);
+    x1.z = fmaf(dt, v1.z, x1.z);
+    x1.w = fmaf(dt, v1.w, x1.w);
     __builtin_nontemporal_store(x0, xp);
     __builtin_nontemporal_store(x1, xp + 1);
   }

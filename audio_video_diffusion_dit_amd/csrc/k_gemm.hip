@@ -96,7 +96,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
   const int hh = lane >> 5;
   const int n_valid = a.rows.n_valid;
   const int seq_pad = a.rows.seq_pad;
-  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN);
+  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
+                         (EPI == EPI_GATED_F32_TO_F32);
+  constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int tok = m0 + wm * TM + t * 32 + l32;
@@ -139,7 +141,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
             for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
           }
         }
-        if constexpr (EPI == EPI_GATED_TO_F32) {
+        if constexpr (OUT_F32) {
           float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
           *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
         } else {
@@ -471,6 +473,8 @@ static hipError_t gemm_dispatch_epi(const GemmArgs& a, hipStream_t s) {
     case EPI_STORE: return gemm_instance<BM, BN, WM, WN, EPI_STORE, ALIGNED>(a, s);
     case EPI_GATED_TO_F32: return gemm_instance<BM, BN, WM, WN, EPI_GATED_TO_F32, ALIGNED>(a, s);
     case EPI_GATED_F32_IN: return gemm_instance<BM, BN, WM, WN, EPI_GATED_F32_IN, ALIGNED>(a, s);
+    case EPI_GATED_F32_TO_F32:
+      return gemm_instance<BM, BN, WM, WN, EPI_GATED_F32_TO_F32, ALIGNED>(a, s);
     case EPI_SWIGLU: return gemm_instance<BM, BN, WM, WN, EPI_SWIGLU, ALIGNED>(a, s);
     default: return hipErrorInvalidValue;
   }
@@ -480,7 +484,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.N <= 0 || a.K <= 0) return hipErrorInvalidValue;
   // Epilogue vectors are 4 features wide and 8-byte aligned.
   if ((a.ldc & 3) != 0) return hipErrorInvalidValue;
-  const bool gated = a.epilogue == EPI_GATED_TO_F32 || a.epilogue == EPI_GATED_F32_IN;
+  const bool gated = a.epilogue == EPI_GATED_TO_F32 || a.epilogue == EPI_GATED_F32_IN ||
+                     a.epilogue == EPI_GATED_F32_TO_F32;
   if (gated && ((a.N & 3) != 0 || (a.ldr & 3) != 0)) return hipErrorInvalidValue;
   // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
   const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
@@ -500,6 +505,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       case EPI_STORE: hipLaunchKernelGGL(k_gemm_dl<EPI_STORE>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_GATED_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_GATED_F32_IN: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_IN>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      case EPI_GATED_F32_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_dl<EPI_SWIGLU>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       default: return hipErrorInvalidValue;
     }

@@ -45,10 +45,12 @@ struct QkNormRopeArgs {
 };
 hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s);
 
-// x += dt_m * v (skipped when v is null), x_bf16 = bf16(x); tail rows of both set to 0.
+// x += dt_m * v (v bf16, or v_f32 fp32; skipped when both are null), x_bf16 = bf16(x) (skipped
+// when null); tail rows set to 0.
 struct StepArgs {
   float* x;
   const uint16_t* v;
+  const float* v_f32;
   uint16_t* x_bf16;
   RowLayout rows;
   int32_t D;
@@ -62,6 +64,7 @@ enum GemmEpilogue : int32_t {
   EPI_GATED_TO_F32 = 1, // out (fp32) = resid (bf16) + (ada + temb)[mod(m)][chunk][n] * acc
   EPI_SWIGLU = 2,       // out (bf16) = silu(acc_gate) * acc_up, gate row n, up row up_offset + n
   EPI_GATED_F32_IN = 3, // out (bf16) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
+  EPI_GATED_F32_TO_F32 = 4, // out (fp32) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
 };
 struct GemmArgs {
   const uint16_t* A;  // [rows, K] activations, row stride lda

@@ -154,6 +154,15 @@ def linear_sigmas(n_intervals: int) -> np.ndarray:
     return s.astype(np.float32)
 
 
+def shifted_sigmas(n_intervals: int, shift: float) -> np.ndarray:
+    """Non-linear schedule: the linear sigmas time-shifted, s' = shift s / (1 + (shift - 1) s)
+    (float64, stored fp32); s'_0 = 1, s'_N = 0, and shift = 1 gives the linear schedule."""
+    s = linear_sigmas(n_intervals).astype(np.float64)
+    out = shift * s / (1.0 + (shift - 1.0) * s)
+    out[0], out[-1] = 1.0, 0.0
+    return out.astype(np.float32)
+
+
 def timestep_embeddings(rng: np.random.Generator, wl: Workload, sigmas_video: np.ndarray,
                         sigmas_audio: np.ndarray) -> np.ndarray:
     """Per-interval embeddings T_i [N, 2, 6, D] fp32 that vary smoothly with sigma.
@@ -205,15 +214,17 @@ class LoopCase:
 
 
 def loop_case(wl: Workload, seed: int = 0, n_blocks: Optional[int] = None,
-              n_intervals: Optional[int] = None) -> LoopCase:
-    """Draw order: blocks, then x_0, then W_t of the timestep embeddings."""
+              n_intervals: Optional[int] = None, shift_video: float = 1.0,
+              shift_audio: float = 1.0) -> LoopCase:
+    """Draw order: blocks, then x_0, then W_t of the timestep embeddings. Sigmas: linear 1 -> 0
+    per modality, or time-shifted (shifted_sigmas) when a shift is not 1."""
     rng = np.random.Generator(np.random.PCG64(seed))
     nb = wl.n_blocks if n_blocks is None else n_blocks
     n = wl.n_intervals if n_intervals is None else n_intervals
     blocks = [make_block(rng, wl) for _ in range(nb)]
     x0 = make_latent_f32(rng, wl)
-    sv = linear_sigmas(n)
-    sa = linear_sigmas(n)
+    sv = linear_sigmas(n) if shift_video == 1.0 else shifted_sigmas(n, shift_video)
+    sa = linear_sigmas(n) if shift_audio == 1.0 else shifted_sigmas(n, shift_audio)
     temb = timestep_embeddings(rng, wl, sv, sa)
     return LoopCase(wl, blocks, x0, sv, sa, temb)
 

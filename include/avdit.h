@@ -110,8 +110,9 @@ typedef struct {
  *   h [L, D] bf16 (norm1 output), qkv [L, 3D] bf16 (q and k after Q/K norm and RoPE),
  *   attn_out [L, D] bf16, x1 [L, D] fp32 (mid-block residual, kept fp32), h2 [L, D] bf16,
  *   act [L, ffn_ld] bf16 (SwiGLU output, row stride ffn_ld; columns >= ffn undefined),
- *   then the loop buffers (present when n_blocks >= 1): x_bf16, ping, pong, velocity,
- *   each [L, D] bf16. */
+ *   then the loop buffers (present when n_blocks >= 1): x_bf16 [L, D] bf16, then ping, pong,
+ *   velocity, each [L, D] and sized for fp32 (bf16 rows in denoise_loop, fp32 rows in
+ *   denoise_loop_f32). */
 typedef struct {
   size_t h, qkv, attn_out, x1, h2, act, x_bf16, ping, pong, velocity, total;
   int64_t ffn_ld;
@@ -153,6 +154,16 @@ int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
                       const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* The same block with an fp32 residual stream ([P2] "Test Plan" and "Test Result": the
+ * FP32-residual runs): x_in and x_out are dev fp32 [seq_pad, D], 16-byte aligned. RMSNorm 1 reads
+ * the fp32 input and both gated residuals (x1 = x + E[m,2] (o Wo^T), x_out = x1 + E[m,5] (...))
+ * read and write fp32; the matrix operands h, q/k/v, o, h2 and the SwiGLU output stay bf16.
+ * Arguments, workspace, aliasing rules and errors as dit_block_forward. */
+int dit_block_forward_f32(const dit_dims* dims, const dit_layout* layout,
+                          const dit_block_weights* weights, const float* temb, const float* x_in,
+                          float* x_out, int32_t attn_mode, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* Flow-matching Euler update of the fp32 latent ([P3] "Changes Made": optimized scheduler
  * updates with independent modality schedules): for valid rows of modality m,
  * x += dt_m * v; x_bf16 = bf16(x) (the next DiT input). Tail rows of x and x_bf16 are set
@@ -179,6 +190,20 @@ int denoise_loop(const dit_dims* dims, const dit_layout* layout,
                  const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
                  int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
                  void* stream);
+
+/* The cached denoise loop with an fp32 residual stream ([P2] "Test Plan" and "Test Result":
+ * FP32 residuals): on a refresh the stack runs on the fp32 latent x_i itself (no bf16
+ * conversion), the blocks chain through fp32 rows (dit_block_forward_f32) and the retained
+ * velocity is the fp32 output of the last block; the Euler step then uses that fp32 velocity.
+ * The sigma arrays may hold any schedule, a different one per modality ([P3] "Motivation":
+ * independent schedulers). Arguments, workspace (dit_workspace_size with n_blocks >= 1),
+ * request-scoped state and errors as denoise_loop. */
+int denoise_loop_f32(const dit_dims* dims, const dit_layout* layout,
+                     const dit_block_weights* blocks, int32_t n_blocks, int32_t n_intervals,
+                     const float* sigmas_video, const float* sigmas_audio,
+                     const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
+                     int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Batched valid-only / fixed-valid attention ([P1] section 2). For request b, head h and
  * query row i < valid_lens[b]: o = softmax_j(q_i . k_j / sqrt(head_dim)) v_j over

@@ -388,14 +388,17 @@ def euler_step(x, v, modality, dt_video: float, dt_audio: float) -> np.ndarray:
 
 
 def denoise_loop(x0, velocity: Callable[[int, np.ndarray], np.ndarray],
-                 sigmas_video, sigmas_audio, modality, hits: Sequence[bool]):
+                 sigmas_video, sigmas_audio, modality, hits: Sequence[bool],
+                 input_bf16: bool = True):
     """Cached denoise loop over N = len(hits) intervals.
 
     [P1 §3] on a hit the previous DiT-predicted velocity (both modalities) is
     reused and the DiT call is skipped; on a refresh the DiT runs on the current
-    latent, converted to bf16 as the DiT input. Every interval then takes one
-    Euler step x_{i+1} = x_i + (sigma_m[i+1] - sigma_m[i]) v. Returns the final
-    latent and the list of velocities the DiT produced (one per refresh).
+    latent, converted to bf16 as the DiT input (input_bf16=False: the latent
+    itself, the FP32-residual runs of [P2 "Test Plan", "Test Result"]). Every
+    interval then takes one Euler step x_{i+1} = x_i + (sigma_m[i+1] - sigma_m[i]) v
+    with each modality on its own sigma schedule [P3 "Motivation"]. Returns the
+    final latent and the list of velocities the DiT produced (one per refresh).
     """
     x = np.asarray(x0, dtype=F64).copy()
     v = None
@@ -405,7 +408,7 @@ def denoise_loop(x0, velocity: Callable[[int, np.ndarray], np.ndarray],
             if v is None:
                 raise ValueError("a hit before any refresh")
         else:
-            v = np.asarray(velocity(i, bf16_round(x)), dtype=F64)
+            v = np.asarray(velocity(i, bf16_round(x) if input_bf16 else x.copy()), dtype=F64)
             produced.append(v)
         dt_v = F64(sigmas_video[i + 1]) - F64(sigmas_video[i])
         dt_a = F64(sigmas_audio[i + 1]) - F64(sigmas_audio[i])

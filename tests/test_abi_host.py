@@ -108,7 +108,11 @@ def test_workspace_map(N):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert m0.qkv - m0.h >= L * D * 2 and m0.attn_out - m0.qkv >= L * 3 * D * 2
     assert n0 >= m0.act + L * 8192 * 2
-    assert n1 == n0 + 4 * (L * D * 2)
+    # loop buffers: the bf16 copy of the latent, then ping, pong and velocity sized for fp32
+    # rows (the fp32-residual loop keeps them in fp32)
+    assert n1 == n0 + L * D * 2 + 3 * (L * D * 4)
+    assert m1.ping - m1.x_bf16 >= L * D * 2 and m1.pong - m1.ping >= L * D * 4
+    assert m1.velocity - m1.pong >= L * D * 4 and n1 - m1.velocity >= L * D * 4
     _, m = N.dit_workspace_size(N.make_dims(256, 4, 64, 683), N.make_layout(512, 96, 640), 0)
     assert m.ffn_ld == 688
 
@@ -122,6 +126,14 @@ def test_entry_points_reject_invalid_arguments_without_device_work(N):
     big = 1 << 40
     # null weights
     code = N.lib.dit_block_forward(d, lay, null_w, 256, 256, 512, 0, big, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    code = N.lib.dit_block_forward_f32(d, lay, null_w, 256, 256, 1 << 20, 0, big, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    # fp32 block: misaligned fp32 rows, overlapping fp32 input and output (640 x 256 x 4 bytes)
+    code = N.lib.dit_block_forward_f32(d, lay, w, 256, (1 << 20) + 4, 1 << 22, 0, big, ws_need, None)
+    assert code == N.DIT_ERR_INVALID
+    code = N.lib.dit_block_forward_f32(d, lay, w, 256, 1 << 20, (1 << 20) + 640 * 256 * 2, 0, big,
+                                       ws_need, None)
     assert code == N.DIT_ERR_INVALID
     # bad attention mode
     code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 30, 5, big, ws_need, None)
@@ -179,3 +191,14 @@ def test_denoise_loop_rejects_invalid_arguments(N):
     nan_sig = (N.c_float * 50)(*([float("nan")] * 50))
     assert call(args(sv=nan_sig)) == N.DIT_ERR_INVALID
     assert call(args(blocks=(N.DitBlockWeights * 1)(N.DitBlockWeights()))) == N.DIT_ERR_INVALID
+
+    def call_f32(a):
+        return N.lib.denoise_loop_f32(a["dims"], a["lay"], a["blocks"], a["nb"], a["n"], a["sv"],
+                                      a["sa"], a["temb"], a["pol"], a["x"], a["mode"], a["stats"],
+                                      a["ws"], a["wsb"], None)
+
+    assert call_f32(args(nb=0)) == N.DIT_ERR_INVALID
+    assert call_f32(args(wsb=need - 256)) == N.DIT_ERR_WORKSPACE
+    assert call_f32(args(pol=bad)) == N.DIT_ERR_UNSUPPORTED
+    assert call_f32(args(sa=nan_sig)) == N.DIT_ERR_INVALID
+    assert call_f32(args(x=(1 << 20) + 4)) == N.DIT_ERR_INVALID

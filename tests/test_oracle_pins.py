@@ -496,6 +496,39 @@ def test_loop_linear_stub_closed_form():
     assert xN[0, 0] == float(c[-1])
 
 
+def test_loop_unrounded_input_and_nonlinear_schedules_closed_form():
+    # input_bf16=False (fp32 residual stream): the DiT sees the latent itself. A linear stub
+    # v = a x gives x_i = c_i x_0 with c_{i+1} = c_i + dt_m,i a c_{r(i)}, r(i) the last refresh,
+    # here with a different non-linear schedule per modality (time-shifted linear sigmas).
+    from audio_video_diffusion_dit_amd.inputs import shifted_sigmas
+    n = 12
+    sv, sa = shifted_sigmas(n, 3.0), shifted_sigmas(n, 0.5)
+    flags = O.cache_schedule(O.CachePolicy("velocity", 0.0, 1.0, 2, 1), n)
+    assert sum(flags) == n // 2
+    mod = np.array([0, 1, 0])
+    x0 = np.array([[1.0 / 3.0], [-0.7], [0.1]])
+    a = -0.9
+    seen = []
+
+    def vel(i, xb):
+        seen.append(xb.copy())
+        return a * xb
+
+    xN, _ = O.denoise_loop(x0, vel, sv, sa, mod, flags, input_bf16=False)
+    assert seen[0][0, 0] == 1.0 / 3.0          # not rounded to bf16
+    for m, sig in ((0, sv), (1, sa)):
+        c, r_c = 1.0, 1.0
+        for i in range(n):
+            if not flags[i]:
+                r_c = c
+            c = c + (float(sig[i + 1]) - float(sig[i])) * a * r_c
+        rows = np.nonzero(mod == m)[0]
+        assert np.allclose(xN[rows, 0], c * x0[rows, 0], rtol=1e-13, atol=0)
+    # the rounded-input loop differs on this non-dyadic latent
+    xb, _ = O.denoise_loop(x0, lambda i, x: a * x, sv, sa, mod, flags)
+    assert not np.array_equal(xb, xN)
+
+
 def test_euler_per_modality_dt():
     x = np.array([[1.0], [1.0], [1.0]])
     v = np.array([[2.0], [2.0], [2.0]])
