@@ -62,7 +62,7 @@ class Layout:
 
 @dataclass(frozen=True)
 class CachePolicy:
-    mode: str = "off"  # "off" or "velocity" ("conservative" is an alias)
+    mode: str = "off"  # "off", "velocity" ("conservative" is an alias) or "extrapolate"
     start_ratio: float = 0.2
     end_ratio: float = 0.8
     refresh_interval: int = 2
@@ -331,8 +331,8 @@ def useful_block_flops(n_valid: int, hidden: int, ffn: int) -> float:
 
 def _policy_enabled(policy: CachePolicy) -> bool:
     mode = policy.mode.lower()
-    if mode == "conservative":
-        mode = "velocity"
+    if mode in ("conservative", "extrapolate"):
+        mode = "velocity"   # the extrapolating mode reuses on exactly the same intervals
     if mode not in ("off", "velocity"):
         raise ValueError(f"unknown cache mode {policy.mode!r}")
     if policy.threshold is not None:
@@ -387,9 +387,24 @@ def euler_step(x, v, modality, dt_video: float, dt_audio: float) -> np.ndarray:
     return out
 
 
+def reused_velocity(i: int, v_last, r_last: int, v_prev, r_prev: Optional[int]) -> np.ndarray:
+    """Velocity used on a reused interval i with first-order extrapolation.
+
+    [P2 "Purpose", "Test Result"]: the pages' cache policies include an order-1 TaylorSeer
+    predictor. Read at the velocity level: with refreshes r_prev < r_last before i, the
+    velocity is continued linearly in the interval index,
+    v_last + (i - r_last) / (r_last - r_prev) * (v_last - v_prev);
+    with a single refresh so far it is plain reuse of v_last.
+    """
+    if v_prev is None or r_prev is None:
+        return v_last
+    lam = F64(i - r_last) / F64(r_last - r_prev)
+    return v_last + lam * (v_last - v_prev)
+
+
 def denoise_loop(x0, velocity: Callable[[int, np.ndarray], np.ndarray],
                  sigmas_video, sigmas_audio, modality, hits: Sequence[bool],
-                 input_bf16: bool = True):
+                 input_bf16: bool = True, extrapolate: bool = False):
     """Cached denoise loop over N = len(hits) intervals.
 
     [P1 §3] on a hit the previous DiT-predicted velocity (both modalities) is
@@ -397,20 +412,27 @@ def denoise_loop(x0, velocity: Callable[[int, np.ndarray], np.ndarray],
     latent, converted to bf16 as the DiT input (input_bf16=False: the latent
     itself, the FP32-residual runs of [P2 "Test Plan", "Test Result"]). Every
     interval then takes one Euler step x_{i+1} = x_i + (sigma_m[i+1] - sigma_m[i]) v
-    with each modality on its own sigma schedule [P3 "Motivation"]. Returns the
-    final latent and the list of velocities the DiT produced (one per refresh).
+    with each modality on its own sigma schedule [P3 "Motivation"]; with
+    extrapolate=True a reused interval takes reused_velocity() instead of the
+    last refresh's velocity. Returns the final latent and the list of velocities
+    the DiT produced (one per refresh).
     """
     x = np.asarray(x0, dtype=F64).copy()
-    v = None
+    v = v_prev = None
+    r = r_prev = None
     produced = []
     for i, hit in enumerate(hits):
         if hit:
             if v is None:
                 raise ValueError("a hit before any refresh")
+            u = reused_velocity(i, v, r, v_prev, r_prev) if extrapolate else v
         else:
+            v_prev, r_prev = v, r
             v = np.asarray(velocity(i, bf16_round(x) if input_bf16 else x.copy()), dtype=F64)
+            r = i
             produced.append(v)
+            u = v
         dt_v = F64(sigmas_video[i + 1]) - F64(sigmas_video[i])
         dt_a = F64(sigmas_audio[i + 1]) - F64(sigmas_audio[i])
-        x = euler_step(x, v, modality, dt_v, dt_a)
+        x = euler_step(x, u, modality, dt_v, dt_a)
     return x, produced

@@ -529,6 +529,39 @@ def test_loop_unrounded_input_and_nonlinear_schedules_closed_form():
     assert not np.array_equal(xb, xN)
 
 
+def test_extrapolated_reuse_is_exact_for_velocities_linear_in_the_interval():
+    # If the DiT velocity is affine in the interval index, v(i) = a + b i, order-1 extrapolation
+    # from two refreshes reproduces it exactly, so the cached loop equals the uncached one (up to
+    # float64 rounding); plain reuse does not. The first hit after the first refresh (only one
+    # velocity known) is plain reuse.
+    n = 30
+    sv = np.linspace(1, 0, n + 1).astype(np.float32)
+    mod = np.array([0, 1])
+    x0 = np.array([[0.3], [-0.2]])
+    a, b = np.array([[1.5], [-0.5]]), np.array([[0.25], [0.125]])
+    vel = lambda i, xb: a + b * i
+    pol = O.CachePolicy("extrapolate", 0.0, 1.0, 3, 2)
+    flags = O.cache_schedule(pol, n)
+    assert flags == O.cache_schedule(O.CachePolicy("velocity", 0.0, 1.0, 3, 2), n)
+    assert flags[1] and flags[2] and not flags[3]          # hits 1, 2 follow a single refresh
+    off, _ = O.denoise_loop(x0, vel, sv, sv, mod, [False] * n)
+    ext, _ = O.denoise_loop(x0, vel, sv, sv, mod, flags, extrapolate=True)
+    reuse, _ = O.denoise_loop(x0, vel, sv, sv, mod, flags)
+    # closed form of the first two hits (plain reuse of v(0)) and exact afterwards
+    dts = np.diff(sv.astype(np.float64))
+    want = x0 + sum(dts[i] * (a + b * (0 if i in (1, 2) else i)) for i in range(n))
+    assert np.allclose(ext, want, rtol=1e-13, atol=1e-15)
+    assert not np.allclose(reuse, want, rtol=1e-6)
+    assert not np.allclose(off, ext, rtol=1e-6)    # differs only by the two early plain reuses
+
+
+def test_reused_velocity_formula():
+    v1, v0 = np.array([2.0]), np.array([1.0])
+    assert O.reused_velocity(7, v1, 6, None, None) is v1
+    assert O.reused_velocity(7, v1, 6, v0, 4)[0] == 2.0 + 0.5 * 1.0
+    assert O.reused_velocity(9, v1, 6, v0, 5)[0] == 2.0 + 3.0 * 1.0
+
+
 def test_euler_per_modality_dt():
     x = np.array([[1.0], [1.0], [1.0]])
     v = np.array([[2.0], [2.0], [2.0]])
