@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libavdit.so
 
 DIT_OK, DIT_ERR_INVALID, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_DEVICE = 0, -1, -2, -3, -4
 DIT_ATTN_VALID_ONLY, DIT_ATTN_FIXED_VALID = 0, 1
-DIT_CACHE_OFF, DIT_CACHE_VELOCITY = 0, 1
+DIT_CACHE_OFF, DIT_CACHE_VELOCITY, DIT_CACHE_EXTRAPOLATE = 0, 1, 2
 
 EXPORTED = ("dit_last_error", "dit_version", "dit_cache_schedule", "dit_workspace_size",
             "dit_block_forward", "dit_block_forward_f32", "step_update", "denoise_loop",
@@ -55,7 +55,8 @@ class DitLoopStats(ctypes.Structure):
 
 class DitWorkspaceMap(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("h", "qkv", "attn_out", "x1", "h2", "act", "x_bf16",
-                                         "ping", "pong", "velocity", "total")] + [("ffn_ld", c_int64)]
+                                         "ping", "pong", "velocity", "velocity_prev", "total")] + \
+        [("ffn_ld", c_int64)]
 
 
 class AvditError(RuntimeError):
@@ -143,8 +144,9 @@ def make_layout(n_video, n_audio, seq_pad, positions=None) -> DitLayout:
 
 
 def resolve_mode(mode: str = "off", quality: str | None = None) -> int:
-    """'off' | 'velocity' | 'conservative' (alias of velocity); quality='high' disables
-    the cache (1Cat-vLLM PR #584, "Purpose")."""
+    """'off' | 'velocity' | 'conservative' (alias of velocity) | 'extrapolate' (same schedule,
+    first-order continued velocity on reused intervals); quality='high' disables the cache
+    (1Cat-vLLM PR #584, "Purpose")."""
     if quality is not None and quality.lower() == "high":
         return DIT_CACHE_OFF
     m = mode.lower()
@@ -152,6 +154,8 @@ def resolve_mode(mode: str = "off", quality: str | None = None) -> int:
         return DIT_CACHE_OFF
     if m in ("velocity", "conservative"):
         return DIT_CACHE_VELOCITY
+    if m == "extrapolate":
+        return DIT_CACHE_EXTRAPOLATE
     raise ValueError(f"unknown cache mode {mode!r}")
 
 

@@ -71,7 +71,7 @@ int check_layout(const dit_layout* l) {
 
 int check_policy(const dit_cache_policy* p) {
   if (!p) return fail(DIT_ERR_INVALID, "policy is null");
-  if (p->mode != DIT_CACHE_OFF && p->mode != DIT_CACHE_VELOCITY)
+  if (p->mode != DIT_CACHE_OFF && p->mode != DIT_CACHE_VELOCITY && p->mode != DIT_CACHE_EXTRAPOLATE)
     return fail(DIT_ERR_UNSUPPORTED, "cache mode %d is not supported", p->mode);
   if (!(p->start_ratio >= 0.0 && p->start_ratio <= 1.0) ||
       !(p->end_ratio >= 0.0 && p->end_ratio <= 1.0))
@@ -132,8 +132,9 @@ void build_map(const dit_dims* d, const dit_layout* l, int32_t n_blocks, dit_wor
     m->ping = off; off += row_f;
     m->pong = off; off += row_f;
     m->velocity = off; off += row_f;
+    m->velocity_prev = off; off += row_f;
   } else {
-    m->x_bf16 = m->ping = m->pong = m->velocity = 0;
+    m->x_bf16 = m->ping = m->pong = m->velocity = m->velocity_prev = 0;
   }
   m->total = off < kAlign ? kAlign : off;
 }
@@ -390,7 +391,12 @@ int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_we
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);
     uint16_t* x_bf16 = reinterpret_cast<uint16_t*>(base + m.x_bf16);
-    void* vel = base + m.velocity;
+    // the velocity of the last refresh lives in vel_buf[cur]; with extrapolation the one before
+    // it is kept in the other buffer (request-scoped state, gone when this call returns)
+    void* vel_buf[2] = {base + m.velocity, base + m.velocity_prev};
+    int cur = 0;
+    int32_t r_last = -1, r_prev = -1;
+    const bool extrap = policy->mode == DIT_CACHE_EXTRAPOLATE;
     void* pp[2] = {base + m.ping, base + m.pong};
     const avdit::RowLayout rows{layout->n_video, layout->n_video + layout->n_audio, layout->seq_pad};
     const size_t temb_step = (size_t)dims->n_mod * 6 * dims->hidden;
@@ -403,6 +409,10 @@ int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_we
       return st;
     for (int32_t i = 0; i < n_intervals; ++i) {
       if (!hits[i]) {
+        if (extrap && r_last >= 0) cur ^= 1;   // keep the previous refresh's velocity
+        r_prev = r_last;
+        r_last = i;
+        void* vel = vel_buf[cur];
         const float* temb_i = temb_steps + (size_t)i * temb_step;
         for (int32_t b = 0; b < n_blocks; ++b) {
           // the fp32 loop feeds the latent itself to the first block
@@ -416,9 +426,17 @@ int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_we
       avdit::StepArgs a{};
       a.x = x_latent;
       if (f32)
-        a.v_f32 = static_cast<const float*>(vel);
+        a.v_f32 = static_cast<const float*>(vel_buf[cur]);
       else
-        a.v = static_cast<const uint16_t*>(vel);
+        a.v = static_cast<const uint16_t*>(vel_buf[cur]);
+      if (hits[i] && extrap && r_prev >= 0) {
+        // first-order extrapolation in the interval index from refreshes r_prev < r_last
+        a.lambda = (float)((double)(i - r_last) / (double)(r_last - r_prev));
+        if (f32)
+          a.v_prev_f32 = static_cast<const float*>(vel_buf[cur ^ 1]);
+        else
+          a.v_prev = static_cast<const uint16_t*>(vel_buf[cur ^ 1]);
+      }
       a.x_bf16 = (!f32 && i + 1 < n_intervals) ? x_bf16 : nullptr;
       a.rows = rows; a.D = dims->hidden;
       a.dt_video = sigmas_video[i + 1] - sigmas_video[i];

@@ -318,6 +318,25 @@ __global__ __launch_bounds__(256) void k_step_update(StepArgs a) {
       v0 = __builtin_nontemporal_load(vp);
       v1 = __builtin_nontemporal_load(vp + 1);
     }
+    if (a.v_prev || a.v_prev_f32) {
+      // first-order extrapolation from the last two refreshes: u = v + lambda (v - v_prev)
+      f32x4 p0, p1;
+      if (a.v_prev) {
+        const u32x4 pp = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.v_prev + (size_t)row * a.D + 8 * c));
+        p0 = f32x4{bf_lo(pp.x), bf_hi(pp.x), bf_lo(pp.y), bf_hi(pp.y)};
+        p1 = f32x4{bf_lo(pp.z), bf_hi(pp.z), bf_lo(pp.w), bf_hi(pp.w)};
+      } else {
+        const f32x4* pq = reinterpret_cast<const f32x4*>(a.v_prev_f32 + (size_t)row * a.D + 8 * c);
+        p0 = __builtin_nontemporal_load(pq);
+        p1 = __builtin_nontemporal_load(pq + 1);
+      }
+      const float l = a.lambda;
+      v0 = f32x4{fmaf(l, v0.x - p0.x, v0.x), fmaf(l, v0.y - p0.y, v0.y),
+                 fmaf(l, v0.z - p0.z, v0.z), fmaf(l, v0.w - p0.w, v0.w)};
+      v1 = f32x4{fmaf(l, v1.x - p1.x, v1.x), fmaf(l, v1.y - p1.y, v1.y),
+                 fmaf(l, v1.z - p1.z, v1.z), fmaf(l, v1.w - p1.w, v1.w)};
+    }
     x0.x = fmaf(dt, v0.x, x0.x);
     x0.y = fmaf(dt, v0.y, x0.y);
     x0.z = fmaf(dt, v0.z, x0.z);

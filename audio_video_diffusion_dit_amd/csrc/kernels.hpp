@@ -45,12 +45,16 @@ struct QkNormRopeArgs {
 };
 hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s);
 
-// x += dt_m * v (v bf16, or v_f32 fp32; skipped when both are null), x_bf16 = bf16(x) (skipped
-// when null); tail rows set to 0.
+// x += dt_m * u (skipped when v and v_f32 are null), x_bf16 = bf16(x) (skipped when null); tail
+// rows set to 0. u = v (bf16, or v_f32 fp32), or, when an older velocity v_prev / v_prev_f32 is
+// given, the extrapolation u = v + lambda (v - v_prev).
 struct StepArgs {
   float* x;
   const uint16_t* v;
   const float* v_f32;
+  const uint16_t* v_prev;
+  const float* v_prev_f32;
+  float lambda;
   uint16_t* x_bf16;
   RowLayout rows;
   int32_t D;

@@ -44,7 +44,7 @@ enum {
 };
 
 enum { DIT_ATTN_VALID_ONLY = 0, DIT_ATTN_FIXED_VALID = 1 };
-enum { DIT_CACHE_OFF = 0, DIT_CACHE_VELOCITY = 1 };
+enum { DIT_CACHE_OFF = 0, DIT_CACHE_VELOCITY = 1, DIT_CACHE_EXTRAPOLATE = 2 };
 
 /* Model dimensions. hidden = heads * head_dim; head_dim is 64 or 128; n_mod is 2 (video,
  * audio). norm_eps is the RMSNorm epsilon of the token norms, qk_eps that of the per-head
@@ -82,11 +82,15 @@ typedef struct {
   const float* ada;
 } dit_block_weights;
 
-/* Velocity-reuse cache policy ([P1] section 3, MiniMaxH3DiTCacheConfig). mode DIT_CACHE_OFF
- * or DIT_CACHE_VELOCITY ("conservative" is an alias resolved by the caller). Reuse happens
- * only for progress i/N in [start_ratio, end_ratio), with a forced refresh every
- * refresh_interval steps and at most max_consecutive_reuse reuses in a row. threshold must
- * be NaN (the pages define only threshold=None). */
+/* Velocity-reuse cache policy ([P1] section 3, MiniMaxH3DiTCacheConfig). mode DIT_CACHE_OFF,
+ * DIT_CACHE_VELOCITY ("conservative" is an alias resolved by the caller) or
+ * DIT_CACHE_EXTRAPOLATE. Reuse happens only for progress i/N in [start_ratio, end_ratio), with a
+ * forced refresh every refresh_interval steps and at most max_consecutive_reuse reuses in a
+ * row. DIT_CACHE_VELOCITY reuses the last refresh's velocity v_r; DIT_CACHE_EXTRAPOLATE reuses
+ * on the same intervals but continues the velocity to first order from the last two refreshes
+ * r' < r, v_r + (i - r) / (r - r') (v_r - v_r') (plain reuse while only one refresh exists; a
+ * velocity-level reading of the order-1 TaylorSeer predictor, [P2] "Purpose", "Test
+ * Result"). threshold must be NaN (the pages define only threshold=None). */
 typedef struct {
   int32_t mode;
   double start_ratio, end_ratio;
@@ -111,10 +115,11 @@ typedef struct {
  *   attn_out [L, D] bf16, x1 [L, D] fp32 (mid-block residual, kept fp32), h2 [L, D] bf16,
  *   act [L, ffn_ld] bf16 (SwiGLU output, row stride ffn_ld; columns >= ffn undefined),
  *   then the loop buffers (present when n_blocks >= 1): x_bf16 [L, D] bf16, then ping, pong,
- *   velocity, each [L, D] and sized for fp32 (bf16 rows in denoise_loop, fp32 rows in
- *   denoise_loop_f32). */
+ *   velocity, velocity_prev, each [L, D] and sized for fp32 (bf16 rows in denoise_loop, fp32
+ *   rows in denoise_loop_f32; velocity_prev holds the older refresh's velocity under
+ *   DIT_CACHE_EXTRAPOLATE, the two velocity buffers alternating). */
 typedef struct {
-  size_t h, qkv, attn_out, x1, h2, act, x_bf16, ping, pong, velocity, total;
+  size_t h, qkv, attn_out, x1, h2, act, x_bf16, ping, pong, velocity, velocity_prev, total;
   int64_t ffn_ld;
 } dit_workspace_map;
 

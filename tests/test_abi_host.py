@@ -48,6 +48,15 @@ def test_schedule_matches_oracle(N, r, c):
     assert off == [False] * 49
 
 
+def test_extrapolate_mode_has_the_reuse_schedule(N):
+    for s, e in RATIOS:
+        for r, c in ((2, 1), (3, 2), (4, 9)):
+            for n in (0, 1, 7, 49, 100):
+                ext = N.dit_cache_schedule(N.make_policy("extrapolate", s, e, r, c), n)
+                assert ext == N.dit_cache_schedule(N.make_policy("velocity", s, e, r, c), n)
+                assert ext == O.cache_schedule(O.CachePolicy("extrapolate", s, e, r, c), n)
+
+
 def test_schedule_counts_printed_on_pages(N):
     hits = N.dit_cache_schedule(N.make_policy("conservative"), 49)
     assert (49 - sum(hits), sum(hits)) == (34, 15)
@@ -110,9 +119,10 @@ def test_workspace_map(N):
     assert n0 >= m0.act + L * 8192 * 2
     # loop buffers: the bf16 copy of the latent, then ping, pong and velocity sized for fp32
     # rows (the fp32-residual loop keeps them in fp32)
-    assert n1 == n0 + L * D * 2 + 3 * (L * D * 4)
+    assert n1 == n0 + L * D * 2 + 4 * (L * D * 4)
     assert m1.ping - m1.x_bf16 >= L * D * 2 and m1.pong - m1.ping >= L * D * 4
-    assert m1.velocity - m1.pong >= L * D * 4 and n1 - m1.velocity >= L * D * 4
+    assert m1.velocity - m1.pong >= L * D * 4 and m1.velocity_prev - m1.velocity >= L * D * 4
+    assert n1 - m1.velocity_prev >= L * D * 4
     _, m = N.dit_workspace_size(N.make_dims(256, 4, 64, 683), N.make_layout(512, 96, 640), 0)
     assert m.ffn_ld == 688
 
