@@ -21,8 +21,9 @@ DIT_ATTN_VALID_ONLY, DIT_ATTN_FIXED_VALID = 0, 1
 DIT_CACHE_OFF, DIT_CACHE_VELOCITY, DIT_CACHE_EXTRAPOLATE = 0, 1, 2
 
 EXPORTED = ("dit_last_error", "dit_version", "dit_cache_schedule", "dit_workspace_size",
-            "dit_block_forward", "dit_block_forward_f32", "step_update", "denoise_loop",
-            "denoise_loop_f32", "dit_attention_forward")
+            "dit_block_forward", "dit_block_forward_f32", "dit_block_forward_batched",
+            "dit_workspace_size_batched", "step_update", "denoise_loop", "denoise_loop_f32",
+            "dit_attention_forward")
 
 
 class DitDims(ctypes.Structure):
@@ -83,6 +84,13 @@ def _load():
     lib.dit_block_forward.argtypes = [POINTER(DitDims), POINTER(DitLayout), POINTER(DitBlockWeights),
                                       c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                       c_void_p]
+    lib.dit_workspace_size_batched.restype = c_size_t
+    lib.dit_workspace_size_batched.argtypes = [POINTER(DitDims), POINTER(DitLayout), c_int32,
+                                               POINTER(DitWorkspaceMap)]
+    lib.dit_block_forward_batched.restype = c_int32
+    lib.dit_block_forward_batched.argtypes = [POINTER(DitDims), POINTER(DitLayout), c_int32,
+                                              POINTER(DitBlockWeights), c_void_p, c_void_p,
+                                              c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
     lib.dit_block_forward_f32.restype = c_int32
     lib.dit_block_forward_f32.argtypes = lib.dit_block_forward.argtypes
     lib.step_update.restype = c_int32
@@ -194,6 +202,28 @@ def dit_block_forward(dims, layout, weights: DitBlockWeights, temb, x_in, x_out,
     _check(lib.dit_block_forward(ctypes.byref(dims), ctypes.byref(layout), ctypes.byref(weights),
                                  _ptr(temb), _ptr(x_in), _ptr(x_out), attn_mode, _ptr(ws), ws_bytes,
                                  _stream(stream)), "dit_block_forward")
+
+
+def dit_workspace_size_batched(dims: DitDims, layouts):
+    """layouts: list of DitLayout (one per request). Returns (bytes, DitWorkspaceMap)."""
+    arr = (DitLayout * len(layouts))(*layouts)
+    m = DitWorkspaceMap()
+    n = lib.dit_workspace_size_batched(ctypes.byref(dims), arr, len(layouts), ctypes.byref(m))
+    if n == 0:
+        raise AvditError(DIT_ERR_INVALID, "dit_workspace_size_batched", last_error())
+    return n, m
+
+
+def dit_block_forward_batched(dims, layouts, weights: DitBlockWeights, temb, x_in, x_out,
+                              attn_mode=DIT_ATTN_VALID_ONLY, ws=None, ws_bytes=None, stream=None):
+    """layouts: list of DitLayout sharing seq_pad; temb: [batch, n_mod, 6, D] fp32;
+    x_in, x_out: [batch * seq_pad, hidden] bf16."""
+    arr = (DitLayout * len(layouts))(*layouts)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib.dit_block_forward_batched(ctypes.byref(dims), arr, len(layouts), ctypes.byref(weights),
+                                         _ptr(temb), _ptr(x_in), _ptr(x_out), attn_mode, _ptr(ws),
+                                         ws_bytes, _stream(stream)), "dit_block_forward_batched")
 
 
 def dit_block_forward_f32(dims, layout, weights: DitBlockWeights, temb, x_in, x_out,

@@ -157,15 +157,32 @@ bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
+// Rows of a block call: one request (from its dit_layout) or a batch of requests that share
+// seq_pad, with per-request rotary positions and timestep tables (temb_stride elements apart).
+struct BlockRows {
+  avdit::RowLayout rows{};
+  const int32_t* positions = nullptr;
+  const int32_t* req_positions[avdit::MAX_REQUESTS] = {};
+  int64_t temb_stride = 0;
+};
+
+BlockRows single_rows(const dit_layout* l) {
+  BlockRows r;
+  r.rows = avdit::RowLayout{l->n_video, l->n_video + l->n_audio, l->seq_pad};
+  r.positions = l->positions;
+  return r;
+}
+
 // Enqueue one block on `s`: eight launches, no host synchronisation. x_in and x_out are bf16
 // rows, or fp32 rows when f32 (the fp32 residual stream: norm1 reads fp32, both gated
 // residual epilogues read and write fp32).
-int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weights* w,
+int enqueue_block(const dit_dims* d, const BlockRows& br, const dit_block_weights* w,
                   const float* temb, const void* x_in, void* x_out, int32_t attn_mode,
                   char* ws, const dit_workspace_map& m, hipStream_t s, bool f32 = false) {
   using namespace avdit;
-  const int32_t D = d->hidden, F = d->ffn, L = l->seq_pad;
-  const RowLayout rows{l->n_video, l->n_video + l->n_audio, L};
+  const int32_t D = d->hidden, F = d->ffn, L = br.rows.seq_pad;
+  const RowLayout& rows = br.rows;
+  const int32_t batch = rows.batch > 1 ? rows.batch : 1;
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + m.h);
   uint16_t* qkv = reinterpret_cast<uint16_t*>(ws + m.qkv);
   uint16_t* att = reinterpret_cast<uint16_t*>(ws + m.attn_out);
@@ -177,7 +194,7 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
   NormModArgs n1{};
   n1.x = x_in; n1.h = h; n1.gain = w->norm1_g; n1.ada = w->ada; n1.temb = temb;
   n1.rows = rows; n1.D = D; n1.shift_chunk = 0; n1.scale_chunk = 1; n1.eps = d->norm_eps;
-  n1.x_f32 = f32 ? 1 : 0;
+  n1.x_f32 = f32 ? 1 : 0; n1.temb_stride = br.temb_stride;
   if ((st = device_status(launch_norm_mod(n1, s), "norm1+modulation")) != DIT_OK) return st;
 
   GemmArgs g{};
@@ -186,7 +203,8 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
   if ((st = device_status(launch_gemm(g, s), "qkv projection")) != DIT_OK) return st;
 
   QkNormRopeArgs r{};
-  r.qkv = qkv; r.q_gain = w->q_g; r.k_gain = w->k_g; r.positions = l->positions; r.rows = rows;
+  r.qkv = qkv; r.q_gain = w->q_g; r.k_gain = w->k_g; r.positions = br.positions; r.rows = rows;
+  for (int b = 0; b < MAX_REQUESTS; ++b) r.req_positions[b] = br.req_positions[b];
   r.heads = d->heads; r.head_dim = d->head_dim; r.row_stride = 3 * D; r.eps = d->qk_eps;
   for (int i = 0; i < d->head_dim / 2; ++i)
     r.inv_freq[i] = (float)std::pow((double)d->rope_base, -2.0 * i / (double)d->head_dim);
@@ -196,24 +214,24 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
   at.q = qkv; at.k = qkv + D; at.v = qkv + 2 * D; at.o = att;
   at.batch_stride = (int64_t)L * 3 * D; at.row_stride = 3 * D;
   at.o_batch_stride = (int64_t)L * D; at.o_row_stride = D;
-  at.batch = 1; at.seq_pad = L; at.heads = d->heads; at.head_dim = d->head_dim;
+  at.batch = batch; at.seq_pad = L; at.heads = d->heads; at.head_dim = d->head_dim;
   at.fixed_valid = attn_mode == DIT_ATTN_FIXED_VALID ? 1 : 0;
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
-  at.valid[0] = rows.n_valid;
+  for (int b = 0; b < batch; ++b) at.valid[b] = rows.batch > 1 ? rows.req_valid[b] : rows.n_valid;
   at.q_gain = w->q_g; at.k_gain = w->k_g;  // q, k come out of the Q/K RMSNorm with these gains
   if ((st = device_status(launch_attention(at, s), "attention")) != DIT_OK) return st;
 
   GemmArgs go{};
   go.A = att; go.W = w->w_o; go.C = x1; go.lda = D; go.ldw = D; go.ldc = D; go.N = D; go.K = D;
   go.rows = rows; go.epilogue = f32 ? EPI_GATED_F32_TO_F32 : EPI_GATED_TO_F32; go.resid = x_in;
-  go.ldr = D; go.ada = w->ada;
+  go.ldr = D; go.ada = w->ada; go.temb_stride = br.temb_stride;
   go.temb = temb; go.chunk = 2;
   if ((st = device_status(launch_gemm(go, s), "out projection")) != DIT_OK) return st;
 
   NormModArgs n2{};
   n2.x = x1; n2.h = h2; n2.gain = w->norm2_g; n2.ada = w->ada; n2.temb = temb;
   n2.rows = rows; n2.D = D; n2.shift_chunk = 3; n2.scale_chunk = 4; n2.eps = d->norm_eps;
-  n2.x_f32 = 1;
+  n2.x_f32 = 1; n2.temb_stride = br.temb_stride;
   if ((st = device_status(launch_norm_mod(n2, s), "norm2+modulation")) != DIT_OK) return st;
 
   GemmArgs gu{};
@@ -224,7 +242,7 @@ int enqueue_block(const dit_dims* d, const dit_layout* l, const dit_block_weight
   GemmArgs gd{};
   gd.A = act; gd.W = w->w_down; gd.C = x_out; gd.lda = m.ffn_ld; gd.ldw = F; gd.ldc = D;
   gd.N = D; gd.K = F; gd.rows = rows; gd.epilogue = f32 ? EPI_GATED_F32_TO_F32 : EPI_GATED_F32_IN;
-  gd.resid = x1; gd.ldr = D;
+  gd.resid = x1; gd.ldr = D; gd.temb_stride = br.temb_stride;
   gd.ada = w->ada; gd.temb = temb; gd.chunk = 5;
   if ((st = device_status(launch_gemm(gd, s), "down projection")) != DIT_OK) return st;
   return DIT_OK;
@@ -301,7 +319,7 @@ int block_forward_impl(const dit_dims* dims, const dit_layout* layout,
     return fail(DIT_ERR_INVALID, "x_in or x_out overlaps the workspace");
   if (layout->seq_pad == 0) return DIT_OK;
   (void)hipGetLastError();
-  return enqueue_block(dims, layout, weights, temb, x_in, x_out, attn_mode,
+  return enqueue_block(dims, single_rows(layout), weights, temb, x_in, x_out, attn_mode,
                        static_cast<char*>(ws), m, static_cast<hipStream_t>(stream), f32);
 }
 
@@ -399,6 +417,7 @@ int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_we
     const bool extrap = policy->mode == DIT_CACHE_EXTRAPOLATE;
     void* pp[2] = {base + m.ping, base + m.pong};
     const avdit::RowLayout rows{layout->n_video, layout->n_video + layout->n_audio, layout->seq_pad};
+    const BlockRows brows = single_rows(layout);
     const size_t temb_step = (size_t)dims->n_mod * 6 * dims->hidden;
 
     // zero the latent's tail rows; the bf16 loop also takes the bf16 copy of x_0 (its DiT input)
@@ -418,7 +437,7 @@ int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_we
           // the fp32 loop feeds the latent itself to the first block
           const void* in = b > 0 ? pp[(b - 1) & 1] : (f32 ? (const void*)x_latent : (const void*)x_bf16);
           void* out = b == n_blocks - 1 ? vel : pp[b & 1];
-          if ((st = enqueue_block(dims, layout, &blocks[b], temb_i, in, out, attn_mode, base, m, s,
+          if ((st = enqueue_block(dims, brows, &blocks[b], temb_i, in, out, attn_mode, base, m, s,
                                   f32)) != DIT_OK)
             return st;
         }
@@ -480,6 +499,90 @@ int denoise_loop_f32(const dit_dims* dims, const dit_layout* layout,
                      void* stream) {
   return loop_impl(dims, layout, blocks, n_blocks, n_intervals, sigmas_video, sigmas_audio,
                    temb_steps, policy, x_latent, attn_mode, stats, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validates a batch of request layouts and describes its rows; the combined layout has
+// batch * seq_pad rows.
+int batch_rows(const dit_layout* layouts, int32_t batch, BlockRows* out, dit_layout* combined) {
+  if (!layouts) return fail(DIT_ERR_INVALID, "layouts is null");
+  if (batch < 1 || batch > avdit::MAX_REQUESTS)
+    return fail(DIT_ERR_INVALID, "batch %d outside [1, %d]", batch, (int)avdit::MAX_REQUESTS);
+  int st;
+  for (int b = 0; b < batch; ++b) {
+    if ((st = check_layout(&layouts[b])) != DIT_OK) return st;
+    if (layouts[b].seq_pad != layouts[0].seq_pad)
+      return fail(DIT_ERR_INVALID, "request %d has seq_pad %d, request 0 has %d", b,
+                  layouts[b].seq_pad, layouts[0].seq_pad);
+  }
+  const int32_t L = layouts[0].seq_pad;
+  if (batch > 1 && L % 256 != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "a batch of requests needs seq_pad a multiple of 256 (got %d)", L);
+  if ((int64_t)batch * L > kMaxSeq)
+    return fail(DIT_ERR_INVALID, "batch x seq_pad = %lld rows is too many", (long long)batch * L);
+  if (batch == 1) {
+    *out = single_rows(&layouts[0]);
+  } else {
+    *out = BlockRows{};
+    out->rows.seq_pad = L;
+    out->rows.batch = batch;
+    for (int b = 0; b < batch; ++b) {
+      out->rows.req_video[b] = layouts[b].n_video;
+      out->rows.req_valid[b] = layouts[b].n_video + layouts[b].n_audio;
+      out->req_positions[b] = layouts[b].positions;
+    }
+  }
+  *combined = dit_layout{0, 0, (int32_t)((int64_t)batch * L), nullptr};
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dit_workspace_size_batched(const dit_dims* dims, const dit_layout* layouts, int32_t batch,
+                                  dit_workspace_map* map) {
+  g_err.clear();
+  BlockRows br;
+  dit_layout all;
+  if (check_dims(dims) != DIT_OK || batch_rows(layouts, batch, &br, &all) != DIT_OK) return 0;
+  dit_workspace_map m;
+  build_map(dims, &all, 0, &m);
+  if (map) *map = m;
+  return m.total;
+}
+
+int dit_block_forward_batched(const dit_dims* dims, const dit_layout* layouts, int32_t batch,
+                              const dit_block_weights* weights, const float* temb,
+                              const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st;
+  BlockRows br;
+  dit_layout all;
+  if ((st = check_dims(dims)) != DIT_OK) return st;
+  if ((st = batch_rows(layouts, batch, &br, &all)) != DIT_OK) return st;
+  if ((st = check_weights(weights, 0)) != DIT_OK) return st;
+  if (!temb || !x_in || !x_out) return fail(DIT_ERR_INVALID, "temb, x_in and x_out must be non-null");
+  if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
+    return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
+  dit_workspace_map m;
+  build_map(dims, &all, 0, &m);
+  if ((st = check_ws(ws, ws_bytes, m.total)) != DIT_OK) return st;
+  const size_t act_bytes = (size_t)all.seq_pad * dims->hidden * 2;
+  if (act_bytes > 0 && ranges_overlap(x_in, act_bytes, x_out, act_bytes))
+    return fail(DIT_ERR_INVALID, "x_in and x_out overlap");
+  if (act_bytes > 0 && (ranges_overlap(x_in, act_bytes, ws, m.total) ||
+                        ranges_overlap(x_out, act_bytes, ws, m.total)))
+    return fail(DIT_ERR_INVALID, "x_in or x_out overlaps the workspace");
+  if (all.seq_pad == 0) return DIT_OK;
+  br.temb_stride = (int64_t)dims->n_mod * 6 * dims->hidden;
+  (void)hipGetLastError();
+  return enqueue_block(dims, br, weights, temb, x_in, x_out, attn_mode, static_cast<char*>(ws), m,
+                       static_cast<hipStream_t>(stream));
 }
 
 int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,

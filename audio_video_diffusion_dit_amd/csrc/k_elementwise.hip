@@ -74,31 +74,33 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
   const float inv_d = 1.0f / (float)D;
   float mul[CPL][8];
   float add[CPL][8];
-  int cur = -1;
+  int cur = -1;   // (request, modality) whose modulation the registers hold
+  const int rows_total = total_rows(a.rows);
   const int row0 = wave * kNormRowsPerWave;
-  if (row0 >= a.rows.seq_pad) return;
+  if (row0 >= rows_total) return;
 
   // software pipeline: the next row's loads are in flight while the current row is reduced
   RowChunk<F32IN> buf[CPL], nxt[CPL];
-  if (row0 < a.rows.n_valid) load_row<CPL, F32IN>(a, row0, lane, nchunk, buf);
+  if (row_info(a.rows, row0).valid) load_row<CPL, F32IN>(a, row0, lane, nchunk, buf);
   for (int rr = 0; rr < kNormRowsPerWave; ++rr) {
     const int row = row0 + rr;
-    if (row >= a.rows.seq_pad) return;
-    if (rr + 1 < kNormRowsPerWave && row + 1 < a.rows.n_valid)
+    if (row >= rows_total) return;
+    const RowInfo ri = row_info(a.rows, row);
+    if (rr + 1 < kNormRowsPerWave && row + 1 < rows_total && row_info(a.rows, row + 1).valid)
       load_row<CPL, F32IN>(a, row + 1, lane, nchunk, nxt);
     uint4* out = reinterpret_cast<uint4*>(a.h + (size_t)row * D);
-    if (row >= a.rows.n_valid) {
+    if (!ri.valid) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
         if (c < nchunk) out[c] = zero4();
       }
     } else {
-      const int m = row < a.rows.n_video ? 0 : 1;
-      if (m != cur) {
-        cur = m;
+      const int m = ri.mod;
+      if (ri.req * 2 + m != cur) {
+        cur = ri.req * 2 + m;
         const float* A = a.ada + (size_t)m * 6 * D;
-        const float* T = a.temb + (size_t)m * 6 * D;
+        const float* T = a.temb + ri.req * a.temb_stride + (size_t)m * 6 * D;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
           const int c = lane + 64 * i;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
 
 template <int CPL>
 static hipError_t norm_mod_instance(const NormModArgs& a, hipStream_t s) {
-  const int waves = (a.rows.seq_pad + kNormRowsPerWave - 1) / kNormRowsPerWave;
+  const int waves = (total_rows(a.rows) + kNormRowsPerWave - 1) / kNormRowsPerWave;
   const int blocks = (waves + 3) / 4;
   if (blocks == 0) return hipSuccess;
   if (a.x_f32)
@@ -194,9 +196,12 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
   constexpr int TPB = 256 / G;      // tokens per block
   const int gl = threadIdx.x % G;
   const int token = blockIdx.x * TPB + threadIdx.x / G;
-  if (token >= a.rows.n_valid) return;
+  if (token >= total_rows(a.rows)) return;
+  const RowInfo ri = row_info(a.rows, token);
+  if (!ri.valid) return;
 
-  const float pos = a.positions ? (float)a.positions[token] : (float)token;
+  const int32_t* positions = a.rows.batch > 1 ? a.req_positions[ri.req] : a.positions;
+  const float pos = positions ? (float)positions[ri.idx] : (float)ri.idx;
   const int gg = gl % HALF_G;       // frequency block of this lane: i = 8 * gg + e
   float inv[8];
 #pragma unroll
@@ -267,7 +272,8 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
 
 hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s) {
   if ((a.row_stride & 7) != 0) return hipErrorInvalidValue;
-  const int n = a.rows.n_valid;
+  // one request: the valid rows; a batch: every row (invalid ones return at once)
+  const int n = a.rows.batch > 1 ? total_rows(a.rows) : a.rows.n_valid;
   if (n <= 0) return hipSuccess;
   if (a.head_dim == 128) {
     const int tpb = 256 / 16;

@@ -87,24 +87,24 @@ __device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_
 
 // Fused epilogue of one wave's accumulator block: lane (l32, hh) holds features fb..fb+3 of
 // token m0 + wm TM + 32 t + l32 in acc[f][t][4 j .. 4 j + 3], fb = n0 + wn (OUT_T 32) + 32 f +
-// 8 j + 4 hh (SwiGLU pairs gate sub-tile 2 f with up sub-tile 2 f + 1). Rows at or past n_valid
-// are written 0, rows past seq_pad are not written.
+// 8 j + 4 hh (SwiGLU pairs gate sub-tile 2 f with up sub-tile 2 f + 1). Invalid rows (at or past
+// a request's valid length) are written 0, rows past the last request are not written.
 template <int EPI, int FT, int MT, int TM, int TN>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][MT], int m0, int n0,
                                            int wm, int wn, int lane) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int n_valid = a.rows.n_valid;
-  const int seq_pad = a.rows.seq_pad;
+  const int rows_total = total_rows(a.rows);
   constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
                          (EPI == EPI_GATED_F32_TO_F32);
   constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int tok = m0 + wm * TM + t * 32 + l32;
-    if (tok >= seq_pad) continue;
-    const bool valid = tok < n_valid;
-    const int mod = tok < a.rows.n_video ? 0 : 1;
+    if (tok >= rows_total) continue;
+    const RowInfo ri = row_info(a.rows, tok);
+    const bool valid = ri.valid;
+    const int mod = ri.mod;
     constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
 #pragma unroll
     for (int f = 0; f < OUT_T; ++f) {
@@ -131,7 +131,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
             }
             const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
             const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
-            const float4 gt = *reinterpret_cast<const float4*>(a.temb + goff);
+            const float4 gt = *reinterpret_cast<const float4*>(a.temb + ri.req * a.temb_stride + goff);
             o[0] = fmaf(ga.x + gt.x, acc[f][t][4 * j + 0], r[0]);
             o[1] = fmaf(ga.y + gt.y, acc[f][t][4 * j + 1], r[1]);
             o[2] = fmaf(ga.z + gt.z, acc[f][t][4 * j + 2], r[2]);
@@ -187,8 +187,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
   select_tile(tiles_m, tiles_n, tile_m, tile_n);
 
   const int m0 = tile_m * BM;
-  const int n_valid = a.rows.n_valid;
-  const int seq_pad = a.rows.seq_pad;
+  const int rows_total = total_rows(a.rows);
   // first output feature of this tile (SwiGLU tiles cover BN/2 outputs)
   const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
 
@@ -200,11 +199,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.0f;
 
-  if (m0 < n_valid) {
+  if (rows_have_valid(a.rows, m0)) {
     const int ck = tid & 7;
     const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
     const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A, (uint32_t)((int64_t)seq_pad * a.lda * 2));
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A, (uint32_t)((int64_t)rows_total * a.lda * 2));
     // byte offset of each staged row (kOob when the row is masked)
     uint32_t src_off[PT];
     int src_row[PT];
@@ -228,7 +227,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
       } else {
         const int tok = m0 + (r - BN);
         src_row[i] = tok;
-        src_ok[i] = tok < n_valid;
+        src_ok[i] = tok < rows_total && row_info(a.rows, tok).valid;
         src_off[i] = src_ok[i] ? (uint32_t)((int64_t)tok * a.lda * 2) : kOob;
       }
     }
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
   int tile_m, tile_n;
   select_tile(tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
-  const int n_valid = a.rows.n_valid;
+  const int rows_total = total_rows(a.rows);
   const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
   f32x16 acc[FT][MT];
 #pragma unroll
@@ -362,10 +361,10 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.0f;
-  if (m0 < n_valid) {
+  if (rows_have_valid(a.rows, m0)) {
     const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
     const i32x4 rs_w = raw_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
-    const i32x4 rs_a = raw_rsrc(a.A, (uint32_t)((int64_t)a.rows.seq_pad * a.lda * 2));
+    const i32x4 rs_a = raw_rsrc(a.A, (uint32_t)((int64_t)rows_total * a.lda * 2));
     uint32_t goff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -384,7 +383,8 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
         goff[i] = feat < a.N ? (uint32_t)((int64_t)wrow * a.ldw * 2 + kc * 16) : kOob;
       } else {
         const int tok = m0 + (r - BN);
-        goff[i] = tok < n_valid ? (uint32_t)((int64_t)tok * a.lda * 2 + kc * 16) : kOob;
+        goff[i] = (tok < rows_total && row_info(a.rows, tok).valid)
+                      ? (uint32_t)((int64_t)tok * a.lda * 2 + kc * 16) : kOob;
       }
     }
     lds_char_t* lds = (lds_char_t*)(lds_ring);
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
 template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
 static hipError_t gemm_instance(const GemmArgs& a, hipStream_t s) {
   const int out_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int tiles_m = (a.rows.seq_pad + BM - 1) / BM;
+  const int tiles_m = (total_rows(a.rows) + BM - 1) / BM;
   const int tiles_n = (a.N + out_per_tile - 1) / out_per_tile;
   const int nt = tiles_m * tiles_n;
   if (nt == 0) return hipSuccess;
@@ -489,16 +489,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (gated && ((a.N & 3) != 0 || (a.ldr & 3) != 0)) return hipErrorInvalidValue;
   // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
   const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
-  if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)a.rows.seq_pad * a.lda * 2 >= (int64_t)kOob)
+  if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)total_rows(a.rows) * a.lda * 2 >= (int64_t)kOob)
     return hipErrorInvalidValue;
+  // a batch of requests: tiles of 256 (or 128) rows must not straddle two requests
+  if (a.rows.batch > 1 && (a.rows.seq_pad % 256) != 0) return hipErrorInvalidValue;
   const bool aligned = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&
                        ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
                        ((reinterpret_cast<uintptr_t>(a.W) & 15) == 0);
   const int out_big = (a.epilogue == EPI_SWIGLU) ? 128 : 256;
-  const long tiles_big = (long)((a.rows.n_valid + 255) / 256) * ((a.N + out_big - 1) / out_big);
+  long valid_rows = a.rows.n_valid;
+  if (a.rows.batch > 1) {
+    valid_rows = 0;
+    for (int b = 0; b < a.rows.batch; ++b) valid_rows += (a.rows.req_valid[b] + 255) / 256 * 256;
+  }
+  const long tiles_big = (long)((valid_rows + 255) / 256) * ((a.N + out_big - 1) / out_big);
   const bool big = tiles_big >= 512;
   if (aligned && big && (a.K % kDlBK) == 0) {
-    const int tiles_m = (a.rows.seq_pad + 255) / 256;
+    const int tiles_m = (total_rows(a.rows) + 255) / 256;
     const int tiles_n = (a.N + out_big - 1) / out_big;
     const dim3 grid(tiles_m * tiles_n), block(512);
     switch (a.epilogue) {

@@ -10,11 +10,43 @@
 namespace avdit {
 
 // Rows of the packed sequence: [0, n_video) video, [n_video, n_valid) audio, then the tail.
+// A batch of requests (batch > 1) stacks batch sequences of seq_pad rows each, request b with its
+// own req_video[b] and req_valid[b]; n_video and n_valid then play no part.
+enum { MAX_REQUESTS = 64 };
 struct RowLayout {
   int32_t n_video;
   int32_t n_valid;
-  int32_t seq_pad;
+  int32_t seq_pad;   // rows per request
+  int32_t batch;     // 0 or 1: one request; otherwise the number of requests
+  int32_t req_video[MAX_REQUESTS];
+  int32_t req_valid[MAX_REQUESTS];
 };
+
+__host__ __device__ inline int32_t total_rows(const RowLayout& r) {
+  return r.batch > 1 ? r.batch * r.seq_pad : r.seq_pad;
+}
+
+struct RowInfo {
+  int32_t req;    // request
+  int32_t idx;    // row inside the request
+  bool valid;
+  int32_t mod;    // 0 video, 1 audio (valid rows)
+};
+
+__host__ __device__ inline RowInfo row_info(const RowLayout& r, int32_t row) {
+  if (r.batch <= 1) return RowInfo{0, row, row < r.n_valid, row < r.n_video ? 0 : 1};
+  const int32_t b = row / r.seq_pad;
+  const int32_t i = row - b * r.seq_pad;
+  return RowInfo{b, i, i < r.req_valid[b], i < r.req_video[b] ? 0 : 1};
+}
+
+// Whether rows [row0, row0 + n) hold a valid row; for a batch, n divides seq_pad (so the rows
+// belong to one request).
+__host__ __device__ inline bool rows_have_valid(const RowLayout& r, int32_t row0) {
+  if (r.batch <= 1) return row0 < r.n_valid;
+  const int32_t b = row0 / r.seq_pad;
+  return row0 - b * r.seq_pad < r.req_valid[b];
+}
 
 // h = RMSNorm(x) * g * (1 + E[m][scale_chunk]) + E[m][shift_chunk], E = ada + temb.
 struct NormModArgs {
@@ -28,6 +60,7 @@ struct NormModArgs {
   int32_t shift_chunk, scale_chunk;
   float eps;
   int32_t x_f32;      // 1: x is fp32
+  int64_t temb_stride;  // elements between the temb tables of successive requests (batch)
 };
 hipError_t launch_norm_mod(const NormModArgs& a, hipStream_t s);
 
@@ -37,6 +70,7 @@ struct QkNormRopeArgs {
   const float* q_gain;     // [Dh]
   const float* k_gain;     // [Dh]
   const int32_t* positions;  // [seq_pad] or null (position = row)
+  const int32_t* req_positions[MAX_REQUESTS];  // batch: per-request [seq_pad] or null
   RowLayout rows;
   int32_t heads, head_dim;
   int64_t row_stride;      // elements between rows (3D)
@@ -84,6 +118,7 @@ struct GemmArgs {
   const float* temb;      // gated epilogues: [2, 6, N]
   int32_t chunk;          // gated epilogues: modulation chunk of the gate
   int32_t up_offset;      // EPI_SWIGLU: first up row of W (= F)
+  int64_t temb_stride;    // gated epilogues: elements between successive requests' temb tables
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 

@@ -83,6 +83,12 @@ WORKLOADS = {
 ATTN_RAGGED = dict(batch=4, seq_pad=8192, heads=16, head_dim=128,
                    valid=(3000, 5100, 7777, 8192))
 
+# A batch of four ragged requests through one H3-scale block (hidden 3072, 24 x 128 heads, FFN
+# 8192), each padded to 8192 rows, with the attention case's length mix: (n_video, n_audio) per
+# request, audio about 1/16 of the tokens as in the H3 workload.
+BLOCK_RAGGED = dict(hidden=3072, heads=24, head_dim=128, ffn=8192, seq_pad=8192,
+                    requests=((2800, 200), (4800, 300), (7277, 500), (7680, 512)))
+
 
 @dataclass
 class BlockParams:

@@ -240,6 +240,47 @@ def configs_report(args):
                      "note": "extrapolated: dit_calls x blocks x one float64 block (Euler steps negligible)"}})
     del ws, blocks, x, x0
 
+    # ---- a batch of 4 ragged requests through one H3-scale block: batched vs one call each ----
+    log("[configs] batched block")
+    cfg = I.BLOCK_RAGGED
+    L, reqs = cfg["seq_pad"], cfg["requests"]
+    B = len(reqs)
+    wl = I.Workload("block_ragged", cfg["hidden"], cfg["heads"], cfg["head_dim"], cfg["ffn"],
+                    reqs[0][0], reqs[0][1], L)
+    rng = np.random.Generator(np.random.PCG64(3))
+    blk_p = I.make_block(rng, wl)
+    D = wl.hidden
+    xb = np.zeros((B * L, D), np.uint16)
+    for b, (nv, na) in enumerate(reqs):
+        xb[b * L: b * L + nv + na] = I.bf16_bits(rng.standard_normal((nv + na, D), dtype=np.float32))
+    temb_b = rng.standard_normal((B, 2, 6, D), dtype=np.float32)
+    dims, blk = dev.dims_of(wl), dev.upload_block(blk_p)
+    lays = [N.make_layout(nv, na, L) for nv, na in reqs]
+    x, temb = dev.to_dev_bf16(xb), dev.to_dev_f32(temb_b)
+    out = torch.empty_like(x)
+    nbytes, _ = N.dit_workspace_size_batched(dims, lays)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ms_b = gpu_ms(lambda: N.dit_block_forward_batched(dims, lays, blk.weights, temb, x, out,
+                                                      N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
+
+    def singles():
+        for b in range(B):
+            N.dit_block_forward(dims, lays[b], blk.weights, temb[b], x[b * L:(b + 1) * L],
+                                out[b * L:(b + 1) * L], N.DIT_ATTN_VALID_ONLY, ws, stream=stream)
+    ms_s = gpu_ms(singles)
+    fl = sum(block_flops(nv + na, D, wl.ffn) for nv, na in reqs)
+    one = I.BlockCase(wl, [blk_p], xb[:L], temb_b[0])      # wl holds request 0's layout
+    orc = oracle_block(one, 64)
+    emit({"workload": "block_ragged", "kind": "batched block", "batch": B, "seq_pad": L,
+          "hidden": D, "ffn": wl.ffn, "heads": wl.heads, "head_dim": wl.head_dim,
+          "valid": [nv + na for nv, na in reqs], "useful_flops": fl,
+          "gpu": {"batched": {"ms": round(ms_b, 4), "useful_tflops": round(fl / ms_b / 1e9, 2)},
+                  "one_call_per_request": {"ms": round(ms_s, 4),
+                                           "useful_tflops": round(fl / ms_s / 1e9, 2)}},
+          "oracle": {**orc, "value": round(orc["value"], 5),
+                     "sample": "request 0: " + orc["sample"]}})
+    del ws, blk, x, out
+
     # ---- ragged valid-only attention: 4 requests of 8192 rows, 16 heads x 128 ----
     log("[configs] attention ragged")
     B, L, H, Dh = 4, 8192, 16, 128

@@ -159,6 +159,26 @@ int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
                       const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Workspace for dit_block_forward_batched: the workspace of one block over all batch * seq_pad
+ * rows, and its map. Returns 0 with dit_last_error() set for invalid dims or layouts. */
+size_t dit_workspace_size_batched(const dit_dims* dims, const dit_layout* layouts, int32_t batch,
+                                  dit_workspace_map* map);
+
+/* One block over a batch of requests in a single call: every launch covers all requests, the
+ * GEMMs skip the row tiles past each request's valid length, and attention runs per (request,
+ * head) over that request's valid keys only ([P1] section 2: valid-only work over each zero
+ * tail; [P2] "Purpose": requests are independent). layouts: host [batch] (batch <= 64), each
+ * request's n_video, n_audio and positions; all share seq_pad, a multiple of 256 when batch > 1
+ * (DIT_ERR_UNSUPPORTED otherwise). Row b * seq_pad + i of x_in / x_out (dev bf16 [batch * seq_pad,
+ * D]) is row i of request b; temb: dev fp32 [batch, n_mod, 6, D], request b's table at
+ * b * n_mod * 6 * D. Each request's output equals its own dit_block_forward output bit for
+ * bit. Workspace from dit_workspace_size_batched; aliasing rules and errors as
+ * dit_block_forward. */
+int dit_block_forward_batched(const dit_dims* dims, const dit_layout* layouts, int32_t batch,
+                              const dit_block_weights* weights, const float* temb,
+                              const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* The same block with an fp32 residual stream ([P2] "Test Plan" and "Test Result": the
  * FP32-residual runs): x_in and x_out are dev fp32 [seq_pad, D], 16-byte aligned. RMSNorm 1 reads
  * the fp32 input and both gated residuals (x1 = x + E[m,2] (o Wo^T), x_out = x1 + E[m,5] (...))

@@ -127,6 +127,35 @@ def test_workspace_map(N):
     assert m.ffn_ld == 688
 
 
+def test_batched_workspace_and_validation(N):
+    d = N.make_dims(256, 4, 64, 683)
+    one = N.make_layout(512, 96, 768)
+    n1, m1 = N.dit_workspace_size(d, one, 0)
+    nb1, mb1 = N.dit_workspace_size_batched(d, [one])
+    assert (n1, m1.act) == (nb1, mb1.act)
+    lays = [N.make_layout(512, 96, 768), N.make_layout(300, 0, 768), N.make_layout(0, 0, 768)]
+    nb, mb = N.dit_workspace_size_batched(d, lays)
+    n3, _ = N.dit_workspace_size(d, N.make_layout(0, 0, 3 * 768), 0)
+    assert nb == n3 and mb.qkv - mb.h >= 3 * 768 * 256 * 2
+    with pytest.raises(N.AvditError):       # requests must share seq_pad
+        N.dit_workspace_size_batched(d, [N.make_layout(512, 96, 768), N.make_layout(10, 0, 512)])
+    with pytest.raises(N.AvditError):       # a batch needs seq_pad a multiple of 256
+        N.dit_workspace_size_batched(d, [N.make_layout(512, 96, 640)] * 2)
+    with pytest.raises(N.AvditError):       # at most 64 requests
+        N.dit_workspace_size_batched(d, [one] * 65)
+    w = N.DitBlockWeights(*([256] * 9))
+    arr = (N.DitLayout * 2)(*lays[:2])
+    need, _ = N.dit_workspace_size_batched(d, lays[:2])
+    big = 1 << 40
+    f = N.lib.dit_block_forward_batched
+    assert f(d, arr, 2, w, 256, 1 << 20, 1 << 30, 0, big, need - 1, None) == N.DIT_ERR_WORKSPACE
+    assert f(d, arr, 0, w, 256, 1 << 20, 1 << 30, 0, big, need, None) == N.DIT_ERR_INVALID
+    assert f(d, arr, 2, w, 256, 1 << 20, (1 << 20) + 100, 0, big, need, None) == N.DIT_ERR_INVALID
+    assert f(d, arr, 2, N.DitBlockWeights(), 256, 1 << 20, 1 << 30, 0, big, need, None) == N.DIT_ERR_INVALID
+    bad = (N.DitLayout * 2)(N.make_layout(512, 96, 640), N.make_layout(10, 0, 640))
+    assert f(d, bad, 2, w, 256, 1 << 20, 1 << 30, 0, big, need, None) == N.DIT_ERR_UNSUPPORTED
+
+
 def test_entry_points_reject_invalid_arguments_without_device_work(N):
     d = N.make_dims(256, 4, 64, 683)
     lay = N.make_layout(512, 96, 640)
