@@ -19,7 +19,8 @@ Pin status: every function is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute-force scalar loops, special cases or the cache counts the
 pages print, except ``block_forward`` as a whole, whose composition is pinned
 only through its parts and a brute-force scalar re-derivation on a tiny shape
-("parity unpinned" against the pages: they print no numeric example of a block).
+("parity unpinned" against the pages: they print no numeric example of a block), and
+``velocity_head``, pinned by closed forms (one-hot rows, a scale of -1) and scalar loops.
 """
 
 from __future__ import annotations
@@ -314,6 +315,32 @@ def stack_forward(x, blocks: Sequence[dict], temb, dims: Dims, layout: Layout,
     for blk in blocks:
         x = block_forward(x, blk, temb, dims, layout, positions)
     return x
+
+
+# Order of the two rows of the final AdaLN table of one modality.
+HEAD_SHIFT, HEAD_SCALE = range(2)
+
+
+def velocity_head(x, gain, ada, temb, w_out, bias, layout: Layout, eps: float) -> np.ndarray:
+    """Velocity head after the block stack: v [L, C] from the stack output x [L, D].
+
+    [P2 "Test Result"]: the model ends in a final AdaLN layer with a table of its own;
+    [P1 §1]: the DiT predicts the flow-matching velocity of the latent. Reading: per modality m
+    a two-row table E = A + T ([n_mod, 2, D]; row 0 shift, row 1 scale), the same RMSNorm with
+    indexed modulation as the block, h = RMSNorm(x) * g * (1 + scale[m]) + shift[m], then a
+    per-modality linear map with bias, v = h W[m]^T + b[m] (W [n_mod, C, D], b [n_mod, C]).
+    Tail rows of v are 0.
+    """
+    mod = row_modality(layout)
+    E = modulation_rows(ada, temb)
+    h = norm_modulate(x, gain, E, mod, HEAD_SHIFT, HEAD_SCALE, eps)
+    w_out = np.asarray(w_out, dtype=F64)
+    b = np.zeros(w_out.shape[:2]) if bias is None else np.asarray(bias, dtype=F64)
+    v = np.zeros((h.shape[0], w_out.shape[1]), dtype=F64)
+    for m in range(w_out.shape[0]):
+        sel = mod == m
+        v[sel] = linear(h[sel], w_out[m]) + b[m]
+    return v
 
 
 def useful_block_flops(n_valid: int, hidden: int, ffn: int) -> float:

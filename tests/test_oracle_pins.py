@@ -567,3 +567,82 @@ def test_euler_per_modality_dt():
     v = np.array([[2.0], [2.0], [2.0]])
     out = O.euler_step(x, v, np.array([0, 1, -1]), -0.25, -0.5)
     assert np.array_equal(out[:, 0], [0.5, 0.0, 0.0])
+
+
+# ------------------------------------------------------- velocity head -----
+
+def _head_case(rng, D=16, C=12, nv=5, na=3, L=10):
+    lay = O.Layout(nv, na, L)
+    x = rng.standard_normal((L, D))
+    g = rng.uniform(0.5, 1.5, D)
+    ada = rng.standard_normal((2, 2, D)) * 0.3
+    temb = rng.standard_normal((2, 2, D)) * 0.3
+    w = rng.standard_normal((2, C, D))
+    b = rng.standard_normal((2, C))
+    return lay, x, g, ada, temb, w, b
+
+
+def test_velocity_head_one_hot_rows_closed_form():
+    """x = c e_j with eps = 0 normalises to sign(c) sqrt(D) e_j, so with zero shift the head
+    returns sign(c) sqrt(D) g_j (1 + scale[m, j]) W[m][:, j] + b[m]: a column of the row's own
+    modality weight (C != D, distinct weights per modality), tails 0."""
+    rng = np.random.default_rng(30)
+    D, C = 16, 12
+    lay, _, g, ada, temb, w, b = _head_case(rng, D, C)
+    ada[:, O.HEAD_SHIFT] = 0.0
+    temb[:, O.HEAD_SHIFT] = 0.0
+    L = lay.seq_pad
+    x = np.zeros((L, D))
+    js = rng.integers(0, D, L)
+    cs = rng.choice([-3.0, -0.5, 0.25, 2.0], L)
+    x[np.arange(L), js] = cs
+    v = O.velocity_head(x, g, ada, temb, w, b, lay, 0.0)
+    assert v.shape == (L, C)
+    for l in range(L):
+        if l >= lay.n_valid:
+            assert np.all(v[l] == 0)
+            continue
+        m = 0 if l < lay.n_video else 1
+        j = js[l]
+        scale = ada[m, O.HEAD_SCALE, j] + temb[m, O.HEAD_SCALE, j]
+        want = math.copysign(1.0, cs[l]) * math.sqrt(D) * g[j] * (1 + scale) * w[m][:, j] + b[m]
+        np.testing.assert_allclose(v[l], want, rtol=1e-12, atol=1e-12)
+
+
+def test_velocity_head_scale_minus_one_gives_shift_projection():
+    """A scale of -1 removes the normalised input: every valid row of modality m returns
+    shift[m] W[m]^T + b[m] whatever x is (this fixes which table row is the shift)."""
+    rng = np.random.default_rng(31)
+    lay, x, g, ada, temb, w, b = _head_case(rng)
+    ada[:, O.HEAD_SCALE] = -1.0
+    temb[:, O.HEAD_SCALE] = 0.0
+    v = O.velocity_head(x, g, ada, temb, w, b, lay, 1e-6)
+    for l in range(lay.n_valid):
+        m = 0 if l < lay.n_video else 1
+        shift = ada[m, O.HEAD_SHIFT] + temb[m, O.HEAD_SHIFT]
+        want = np.array([sum(shift[d] * w[m][c, d] for d in range(len(shift))) + b[m][c]
+                         for c in range(w.shape[1])])
+        np.testing.assert_allclose(v[l], want, rtol=1e-12, atol=1e-12)
+    assert np.all(v[lay.n_valid:] == 0)
+
+
+def test_velocity_head_against_scalar_loops():
+    """Every output element recomputed with scalar loops on a tiny ragged case, no bias."""
+    rng = np.random.default_rng(32)
+    lay, x, g, ada, temb, w, _ = _head_case(rng, D=8, C=5, nv=3, na=4, L=9)
+    eps = 1e-6
+    v = O.velocity_head(x, g, ada, temb, w, None, lay, eps)
+    D, C = x.shape[1], w.shape[1]
+    for l in range(lay.seq_pad):
+        for c in range(C):
+            if l >= lay.n_valid:
+                assert v[l, c] == 0
+                continue
+            m = 0 if l < lay.n_video else 1
+            ms = sum(x[l, d] ** 2 for d in range(D)) / D
+            acc = 0.0
+            for d in range(D):
+                hd = x[l, d] / math.sqrt(ms + eps) * g[d]
+                hd = hd * (1 + ada[m, 1, d] + temb[m, 1, d]) + ada[m, 0, d] + temb[m, 0, d]
+                acc += hd * w[m, c, d]
+            assert abs(v[l, c] - acc) <= 1e-12 * max(1.0, abs(acc))
