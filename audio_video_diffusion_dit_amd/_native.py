@@ -23,7 +23,8 @@ DIT_CACHE_OFF, DIT_CACHE_VELOCITY, DIT_CACHE_EXTRAPOLATE = 0, 1, 2
 EXPORTED = ("dit_last_error", "dit_version", "dit_cache_schedule", "dit_workspace_size",
             "dit_block_forward", "dit_block_forward_f32", "dit_block_forward_batched",
             "dit_workspace_size_batched", "step_update", "denoise_loop", "denoise_loop_f32",
-            "dit_attention_forward")
+            "dit_attention_forward", "dit_head_workspace_size", "dit_velocity_head",
+            "dit_velocity_head_f32")
 
 
 class DitDims(ctypes.Structure):
@@ -40,6 +41,11 @@ class DitLayout(ctypes.Structure):
 class DitBlockWeights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("w_qkv", "w_o", "w_gate_up", "w_down", "norm1_g",
                                          "norm2_g", "q_g", "k_g", "ada")]
+
+
+class DitHeadWeights(ctypes.Structure):
+    _fields_ = [("norm_g", c_void_p), ("ada", c_void_p), ("w_out", c_void_p), ("bias", c_void_p),
+                ("out_channels", c_int32)]
 
 
 class DitCachePolicy(ctypes.Structure):
@@ -93,6 +99,13 @@ def _load():
                                               c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
     lib.dit_block_forward_f32.restype = c_int32
     lib.dit_block_forward_f32.argtypes = lib.dit_block_forward.argtypes
+    lib.dit_head_workspace_size.restype = c_size_t
+    lib.dit_head_workspace_size.argtypes = [POINTER(DitDims), POINTER(DitLayout)]
+    lib.dit_velocity_head.restype = c_int32
+    lib.dit_velocity_head.argtypes = [POINTER(DitDims), POINTER(DitLayout), POINTER(DitHeadWeights),
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dit_velocity_head_f32.restype = c_int32
+    lib.dit_velocity_head_f32.argtypes = lib.dit_velocity_head.argtypes
     lib.step_update.restype = c_int32
     lib.step_update.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(DitLayout), c_int32, c_float,
                                 c_float, c_void_p]
@@ -233,6 +246,27 @@ def dit_block_forward_f32(dims, layout, weights: DitBlockWeights, temb, x_in, x_
     _check(lib.dit_block_forward_f32(ctypes.byref(dims), ctypes.byref(layout), ctypes.byref(weights),
                                      _ptr(temb), _ptr(x_in), _ptr(x_out), attn_mode, _ptr(ws),
                                      ws_bytes, _stream(stream)), "dit_block_forward_f32")
+
+
+def dit_head_workspace_size(dims, layout) -> int:
+    n = lib.dit_head_workspace_size(ctypes.byref(dims), ctypes.byref(layout))
+    if n == 0:
+        raise AvditError(DIT_ERR_INVALID, "dit_head_workspace_size", last_error())
+    return n
+
+
+def make_head(norm_g, ada, w_out, bias, out_channels) -> DitHeadWeights:
+    return DitHeadWeights(_ptr(norm_g), _ptr(ada), _ptr(w_out), _ptr(bias), out_channels)
+
+
+def dit_velocity_head(dims, layout, head: DitHeadWeights, temb, x, v, ws=None, ws_bytes=None,
+                      stream=None, x_f32=False):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    name = "dit_velocity_head_f32" if x_f32 else "dit_velocity_head"
+    _check(getattr(lib, name)(ctypes.byref(dims), ctypes.byref(layout), ctypes.byref(head),
+                              _ptr(temb), _ptr(x), _ptr(v), _ptr(ws), ws_bytes, _stream(stream)),
+           name)
 
 
 def step_update(x, v, x_bf16, layout, hidden, dt_video, dt_audio, stream=None):

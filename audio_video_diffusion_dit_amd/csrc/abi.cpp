@@ -630,3 +630,94 @@ int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Velocity head: final RMSNorm with the two-row indexed modulation, then one output
+// projection per modality with an fp32 bias epilogue.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr int32_t kMaxOutChannels = 1 << 16;
+
+size_t head_ws_bytes(const dit_dims* d, const dit_layout* l) {
+  const size_t n = align_up((size_t)l->seq_pad * d->hidden * 2);
+  return n < kAlign ? kAlign : n;
+}
+
+int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_weights* hw,
+              const float* temb, const void* x, float* v, void* ws, size_t ws_bytes,
+              void* stream, bool f32) {
+  using namespace avdit;
+  g_err.clear();
+  int st;
+  if ((st = check_dims(dims)) != DIT_OK) return st;
+  if ((st = check_layout(layout)) != DIT_OK) return st;
+  if (!hw) return fail(DIT_ERR_INVALID, "head weights are null");
+  if (!hw->norm_g || !hw->ada || !hw->w_out)
+    return fail(DIT_ERR_INVALID, "the head has a null weight pointer");
+  const int32_t C = hw->out_channels;
+  if (C <= 0 || (C & 7) != 0 || C > kMaxOutChannels)
+    return fail(DIT_ERR_INVALID, "out_channels %d must be a positive multiple of 8, at most %d", C,
+                kMaxOutChannels);
+  if (((uintptr_t)hw->bias & 15) != 0) return fail(DIT_ERR_INVALID, "bias must be 16-byte aligned");
+  if (!temb || !x || !v) return fail(DIT_ERR_INVALID, "temb, x and v must be non-null");
+  if ((((uintptr_t)x) & 15) || (((uintptr_t)v) & 15))
+    return fail(DIT_ERR_INVALID, "x and v must be 16-byte aligned");
+  const size_t need = head_ws_bytes(dims, layout);
+  if ((st = check_ws(ws, ws_bytes, need)) != DIT_OK) return st;
+  const int32_t D = dims->hidden, L = layout->seq_pad;
+  const int32_t nv = layout->n_video, V = layout->n_video + layout->n_audio;
+  const size_t xb = (size_t)L * D * (f32 ? 4 : 2), vb = (size_t)L * C * 4;
+  if (L > 0 && (ranges_overlap(x, xb, v, vb) || ranges_overlap(x, xb, ws, need) ||
+                ranges_overlap(v, vb, ws, need)))
+    return fail(DIT_ERR_INVALID, "x, v and the workspace must not overlap");
+  if (L == 0) return DIT_OK;
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = static_cast<uint16_t*>(ws);
+
+  NormModArgs n{};
+  n.x = x; n.h = h; n.gain = hw->norm_g; n.ada = hw->ada; n.temb = temb;
+  n.rows = RowLayout{nv, V, L}; n.D = D; n.shift_chunk = 0; n.scale_chunk = 1;
+  n.eps = dims->norm_eps; n.x_f32 = f32 ? 1 : 0; n.temb_stride = 0; n.table_rows = 2;
+  if ((st = device_status(launch_norm_mod(n, s), "final norm+modulation")) != DIT_OK) return st;
+
+  // One launch per modality over its own rows; the audio launch also writes the zero tail.
+  // Row modality inside a launch comes from its RowLayout, which selects the bias row.
+  for (int m = 0; m < 2; ++m) {
+    const int32_t r0 = m == 0 ? 0 : nv;
+    const int32_t rows = m == 0 ? nv : L - nv;
+    if (rows <= 0) continue;
+    GemmArgs g{};
+    g.A = h + (size_t)r0 * D; g.W = hw->w_out + (size_t)m * C * D; g.C = v + (size_t)r0 * C;
+    g.lda = D; g.ldw = D; g.ldc = C; g.N = C; g.K = D;
+    g.rows = m == 0 ? RowLayout{nv, nv, nv} : RowLayout{0, V - nv, L - nv};
+    g.epilogue = EPI_BIAS_TO_F32; g.bias = hw->bias;
+    if ((st = device_status(launch_gemm(g, s), "head projection")) != DIT_OK) return st;
+  }
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout) {
+  g_err.clear();
+  if (check_dims(dims) != DIT_OK || check_layout(layout) != DIT_OK) return 0;
+  return head_ws_bytes(dims, layout);
+}
+
+int dit_velocity_head(const dit_dims* dims, const dit_layout* layout,
+                      const dit_head_weights* head, const float* temb, const uint16_t* x,
+                      float* v, void* ws, size_t ws_bytes, void* stream) {
+  return head_impl(dims, layout, head, temb, x, v, ws, ws_bytes, stream, false);
+}
+
+int dit_velocity_head_f32(const dit_dims* dims, const dit_layout* layout,
+                          const dit_head_weights* head, const float* temb, const float* x,
+                          float* v, void* ws, size_t ws_bytes, void* stream) {
+  return head_impl(dims, layout, head, temb, x, v, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"

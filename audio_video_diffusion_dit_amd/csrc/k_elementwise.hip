@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
       const int m = ri.mod;
       if (ri.req * 2 + m != cur) {
         cur = ri.req * 2 + m;
-        const float* A = a.ada + (size_t)m * 6 * D;
-        const float* T = a.temb + ri.req * a.temb_stride + (size_t)m * 6 * D;
+        const float* A = a.ada + (size_t)m * a.table_rows * D;
+        const float* T = a.temb + ri.req * a.temb_stride + (size_t)m * a.table_rows * D;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
           const int c = lane + 64 * i;

@@ -1,8 +1,9 @@
 // bf16 MFMA GEMM for the block's projections: C[m][n] = sum_k A[m][k] * W[n][k], both operands
 // contiguous along k (activations [tokens, K], weights [out, in]), fp32 accumulation, with the
 // epilogue fused: plain store (QKV), gated residual (out-projection into the fp32 mid-block
-// residual, down-projection from it), or SwiGLU over interleaved gate/up weight rows (gate/up
-// projection; TeleFuser PR #23, "Changes Made": fused SwiGLU).
+// residual, down-projection from it), SwiGLU over interleaved gate/up weight rows (gate/up
+// projection; TeleFuser PR #23, "Changes Made": fused SwiGLU), or an fp32 store with a
+// per-modality bias (the velocity head's output projection).
 //
 // Design for gfx950:
 //  * WM x WN wave64s per workgroup; each wave owns a (BN/WN features) x (BM/WM tokens)
@@ -97,7 +98,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
   const int rows_total = total_rows(a.rows);
   constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
                          (EPI == EPI_GATED_F32_TO_F32);
-  constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
+  constexpr bool OUT_F32 =
+      (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32) || (EPI == EPI_BIAS_TO_F32);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int tok = m0 + wm * TM + t * 32 + l32;
@@ -136,6 +138,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
             o[1] = fmaf(ga.y + gt.y, acc[f][t][4 * j + 1], r[1]);
             o[2] = fmaf(ga.z + gt.z, acc[f][t][4 * j + 2], r[2]);
             o[3] = fmaf(ga.w + gt.w, acc[f][t][4 * j + 3], r[3]);
+          } else if constexpr (EPI == EPI_BIAS_TO_F32) {
+            float4 b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (a.bias) b = *reinterpret_cast<const float4*>(a.bias + (int64_t)mod * a.N + fb);
+            o[0] = acc[f][t][4 * j + 0] + b.x;
+            o[1] = acc[f][t][4 * j + 1] + b.y;
+            o[2] = acc[f][t][4 * j + 2] + b.z;
+            o[3] = acc[f][t][4 * j + 3] + b.w;
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
@@ -476,6 +485,7 @@ static hipError_t gemm_dispatch_epi(const GemmArgs& a, hipStream_t s) {
     case EPI_GATED_F32_TO_F32:
       return gemm_instance<BM, BN, WM, WN, EPI_GATED_F32_TO_F32, ALIGNED>(a, s);
     case EPI_SWIGLU: return gemm_instance<BM, BN, WM, WN, EPI_SWIGLU, ALIGNED>(a, s);
+    case EPI_BIAS_TO_F32: return gemm_instance<BM, BN, WM, WN, EPI_BIAS_TO_F32, ALIGNED>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -487,6 +497,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const bool gated = a.epilogue == EPI_GATED_TO_F32 || a.epilogue == EPI_GATED_F32_IN ||
                      a.epilogue == EPI_GATED_F32_TO_F32;
   if (gated && ((a.N & 3) != 0 || (a.ldr & 3) != 0)) return hipErrorInvalidValue;
+  if (a.epilogue == EPI_BIAS_TO_F32 &&
+      ((a.N & 3) != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 15) != 0))
+    return hipErrorInvalidValue;
   // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
   const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
   if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)total_rows(a.rows) * a.lda * 2 >= (int64_t)kOob)
@@ -514,6 +527,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       case EPI_GATED_F32_IN: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_IN>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_GATED_F32_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_dl<EPI_SWIGLU>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      case EPI_BIAS_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_BIAS_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -53,14 +53,15 @@ struct NormModArgs {
   const void* x;      // [seq_pad, D] bf16, or fp32 when x_f32
   uint16_t* h;        // [seq_pad, D] bf16
   const float* gain;  // [D]
-  const float* ada;   // [2, 6, D]
-  const float* temb;  // [2, 6, D]
+  const float* ada;   // [2, table_rows, D]
+  const float* temb;  // [2, table_rows, D]
   RowLayout rows;
   int32_t D;
   int32_t shift_chunk, scale_chunk;
   float eps;
   int32_t x_f32;      // 1: x is fp32
   int64_t temb_stride;  // elements between the temb tables of successive requests (batch)
+  int32_t table_rows = 6;  // rows per modality of ada/temb: 6 in a block, 2 in the final layer
 };
 hipError_t launch_norm_mod(const NormModArgs& a, hipStream_t s);
 
@@ -103,11 +104,12 @@ enum GemmEpilogue : int32_t {
   EPI_SWIGLU = 2,       // out (bf16) = silu(acc_gate) * acc_up, gate row n, up row up_offset + n
   EPI_GATED_F32_IN = 3, // out (bf16) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
   EPI_GATED_F32_TO_F32 = 4, // out (fp32) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
+  EPI_BIAS_TO_F32 = 5,  // out (fp32) = acc + bias[mod(m)][n] (no bias: acc)
 };
 struct GemmArgs {
   const uint16_t* A;  // [rows, K] activations, row stride lda
   const uint16_t* W;  // [N_w, K] weights, row stride ldw
-  void* C;            // [rows, N] output (bf16, or fp32 for EPI_GATED_TO_F32), row stride ldc
+  void* C;            // [rows, N] output (bf16, or fp32 for the *_TO_F32 epilogues), row stride ldc
   int64_t lda, ldw, ldc;
   int32_t N, K;       // output features, reduction length
   RowLayout rows;     // rows >= n_valid of C are written 0; rows >= seq_pad untouched
@@ -119,6 +121,7 @@ struct GemmArgs {
   int32_t chunk;          // gated epilogues: modulation chunk of the gate
   int32_t up_offset;      // EPI_SWIGLU: first up row of W (= F)
   int64_t temb_stride;    // gated epilogues: elements between successive requests' temb tables
+  const float* bias = nullptr;  // EPI_BIAS_TO_F32: [2, N] per-modality bias, or null
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 

@@ -133,6 +133,35 @@ def make_block(rng: np.random.Generator, wl: Workload, weight_std: float = 0.02,
                        ones_h.copy(), ones_h.copy(), ada.astype(np.float32))
 
 
+# Output channels of the velocity head per token (the latent channels of both modalities); the
+# pages give no channel count.
+HEAD_CHANNELS = 128
+
+
+@dataclass
+class HeadParams:
+    """The velocity head: final norm gain and two-row table, per-modality output projection."""
+    norm_g: np.ndarray  # f32 [D]
+    ada: np.ndarray     # f32 [2, 2, D] (shift, scale)
+    w_out: np.ndarray   # uint16 [2, C, D]
+    bias: np.ndarray    # f32 [2, C]
+
+    def as_float(self) -> dict:
+        return dict(norm_g=self.norm_g, ada=self.ada, w_out=bf16_to_f32(self.w_out), bias=self.bias)
+
+
+def make_head(rng: np.random.Generator, wl: Workload, channels: int = HEAD_CHANNELS,
+              weight_std: float = 0.02) -> HeadParams:
+    """Draw order: w_out (bf16 N(0, 0.02)), ada (fp32 N(0, 0.02)), bias (fp32 N(0, 0.02)),
+    norm gain (fp32 U(0.5, 1.5))."""
+    D = wl.hidden
+    w_out = _normal_bf16(rng, (2, channels, D), weight_std)
+    ada = rng.standard_normal(size=(2, 2, D), dtype=np.float32) * np.float32(0.02)
+    bias = rng.standard_normal(size=(2, channels), dtype=np.float32) * np.float32(0.02)
+    g = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    return HeadParams(g, ada.astype(np.float32), w_out, bias.astype(np.float32))
+
+
 def make_activation_bf16(rng: np.random.Generator, wl: Workload, std: float = 1.0) -> np.ndarray:
     """x [seq_pad, D] bf16 bits: N(0, std) on the valid rows, zero tail."""
     x = np.zeros((wl.seq_pad, wl.hidden), dtype=np.uint16)

@@ -281,6 +281,42 @@ def configs_report(args):
                      "sample": "request 0: " + orc["sample"]}})
     del ws, blk, x, out
 
+    # ---- the velocity head on the 32768-token H3-scale stack output ----
+    log("[configs] velocity head")
+    wl = I.WORKLOADS["loop_8blk_32k"]
+    rng = np.random.Generator(np.random.PCG64(4))
+    hp = I.make_head(rng, wl)
+    C = hp.w_out.shape[1]
+    xh = dev.to_dev_bf16(I.make_activation_bf16(rng, wl))
+    th = dev.to_dev_f32(rng.standard_normal((2, 2, wl.hidden), dtype=np.float32))
+    hw = [dev.to_dev_f32(hp.norm_g), dev.to_dev_f32(hp.ada), dev.to_dev_bf16(hp.w_out),
+          dev.to_dev_f32(hp.bias)]
+    head = N.make_head(*hw, C)
+    dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+    ws = torch.empty(N.dit_head_workspace_size(dims, lay), dtype=torch.uint8, device="cuda")
+    vh = torch.empty((wl.seq_pad, C), dtype=torch.float32, device="cuda")
+    ms = gpu_ms(lambda: N.dit_velocity_head(dims, lay, head, th, xh, vh, ws, stream=stream))
+    V, D, L = wl.n_valid, wl.hidden, wl.seq_pad
+    min_bytes = 2.0 * V * D + 4.0 * L * C + 2.0 * 2 * C * D      # x in, v out, weights
+    run_bytes = min_bytes + 4.0 * V * D                           # + the bf16 h round trip
+    fl = 2.0 * V * D * C
+    t0 = time.perf_counter()
+    rows = np.sort(np.random.default_rng(5).choice(V, 1024, replace=False))
+    xo = I.bf16_to_f32(dev.bf16_bits_of(xh)[rows]).astype(np.float64)
+    hf = hp.as_float()
+    O.velocity_head(xo, hf["norm_g"], hf["ada"], th.cpu().numpy(), hf["w_out"], hf["bias"],
+                    O.Layout(len(rows), 0, len(rows)), 1e-6)
+    dt = time.perf_counter() - t0
+    emit({"workload": "head_32k", "kind": "velocity head", "valid": V, "seq_pad": L, "hidden": D,
+          "channels": C, "gpu_ms": round(ms, 4),
+          "min_hbm_bytes": min_bytes, "kernel_hbm_bytes": run_bytes,
+          "gbps_min": round(min_bytes / ms / 1e6, 1), "gbps_kernels": round(run_bytes / ms / 1e6, 1),
+          "frac_of_8TBs_kernels": round(run_bytes / ms / 1e6 / 8000.0, 4),
+          "useful_tflops": round(fl / ms / 1e9, 2),
+          "oracle": {"seconds": round(dt, 3), "value": round(2.0 * len(rows) * D * C / dt / 1e12, 5),
+                     "unit": "TFLOP/s", "sample": f"{len(rows)} rows (video), whole head"}})
+    del ws, xh, vh, hw
+
     # ---- ragged valid-only attention: 4 requests of 8192 rows, 16 heads x 128 ----
     log("[configs] attention ragged")
     B, L, H, Dh = 4, 8192, 16, 128

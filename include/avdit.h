@@ -123,6 +123,22 @@ typedef struct {
   int64_t ffn_ld;
 } dit_workspace_map;
 
+/* Parameters of the velocity head, all dev: the final AdaLN layer and the output projection
+ * that turn the stack output into the velocity ([P2] "Test Result": the model ends in a final
+ * AdaLN layer with a table of its own; [P1] section 1: the DiT predicts the flow-matching
+ * velocity).
+ *   norm_g [D]; ada [n_mod, 2, D], rows shift then scale;
+ *   w_out bf16 [n_mod, out_channels, D]: one [out, in] matrix per modality;
+ *   bias fp32 [n_mod, out_channels], 16-byte aligned, or NULL for none;
+ *   out_channels: a positive multiple of 8, at most 65536. */
+typedef struct {
+  const float* norm_g;
+  const float* ada;
+  const uint16_t* w_out;
+  const float* bias;
+  int32_t out_channels;
+} dit_head_weights;
+
 /* Last error message of the calling thread ("" if none). Never NULL. */
 const char* dit_last_error(void);
 
@@ -229,6 +245,30 @@ int denoise_loop_f32(const dit_dims* dims, const dit_layout* layout,
                      const float* temb_steps, const dit_cache_policy* policy, float* x_latent,
                      int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Workspace of dit_velocity_head and dit_velocity_head_f32 (the modulated norm, bf16
+ * [seq_pad, D]). A block workspace of the same dims and layout is large enough. Returns 0 with
+ * dit_last_error() set for invalid dims or layout. */
+size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout);
+
+/* Velocity head ([P2] "Test Result", final AdaLN layer; [P1] section 1): for a valid row l of
+ * modality m, h = x_l / sqrt(mean(x_l^2) + norm_eps) * norm_g * (1 + E[m][1]) + E[m][0] with
+ * E = head->ada + temb (the same fused RMSNorm with indexed modulation as the block), then
+ * v_l = h W_m^T + b_m in fp32 (h is rounded to bf16 for the product). Tail rows of v are 0.
+ *   x: dev bf16 [seq_pad, D], the stack output, 16-byte aligned;
+ *   temb: dev fp32 [n_mod, 2, D], the timestep part of the final table;
+ *   v: dev fp32 [seq_pad, out_channels], 16-byte aligned.
+ * x, v and the workspace must not overlap (DIT_ERR_INVALID). Other errors as
+ * dit_block_forward. */
+int dit_velocity_head(const dit_dims* dims, const dit_layout* layout,
+                      const dit_head_weights* head, const float* temb, const uint16_t* x,
+                      float* v, void* ws, size_t ws_bytes, void* stream);
+
+/* The same head on an fp32 stack output (the fp32 residual stream): x dev fp32 [seq_pad, D],
+ * 16-byte aligned. Everything else as dit_velocity_head. */
+int dit_velocity_head_f32(const dit_dims* dims, const dit_layout* layout,
+                          const dit_head_weights* head, const float* temb, const float* x,
+                          float* v, void* ws, size_t ws_bytes, void* stream);
 
 /* Batched valid-only / fixed-valid attention ([P1] section 2). For request b, head h and
  * query row i < valid_lens[b]: o = softmax_j(q_i . k_j / sqrt(head_dim)) v_j over

@@ -241,3 +241,35 @@ def test_denoise_loop_rejects_invalid_arguments(N):
     assert call_f32(args(pol=bad)) == N.DIT_ERR_UNSUPPORTED
     assert call_f32(args(sa=nan_sig)) == N.DIT_ERR_INVALID
     assert call_f32(args(x=(1 << 20) + 4)) == N.DIT_ERR_INVALID
+
+
+def test_head_workspace_and_validation(N):
+    d = N.make_dims(256, 4, 64, 683)
+    lay = N.make_layout(512, 96, 640)
+    need = N.dit_head_workspace_size(d, lay)
+    assert need == 640 * 256 * 2
+    n_blk, _ = N.dit_workspace_size(d, lay, 0)
+    assert n_blk >= need
+    assert N.dit_head_workspace_size(d, N.make_layout(0, 0, 0)) == 256
+    with pytest.raises(N.AvditError):
+        N.dit_head_workspace_size(d, N.make_layout(600, 96, 640))
+    f = N.lib.dit_velocity_head
+    ws, x, v, t = 1 << 30, 1 << 32, 1 << 34, 1 << 20
+    good = N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 64)
+
+    def call(head=good, temb=t, x_=x, v_=v, ws_=ws, nbytes=need, layout=lay):
+        return f(d, layout, head, temb, x_, v_, ws_, nbytes, None)
+
+    assert call(nbytes=need - 1) == N.DIT_ERR_WORKSPACE
+    assert call(head=N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 60)) == N.DIT_ERR_INVALID
+    assert call(head=N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 0)) == N.DIT_ERR_INVALID
+    assert call(head=N.DitHeadWeights(256, 512, None, 1 << 25, 64)) == N.DIT_ERR_INVALID
+    assert call(head=N.DitHeadWeights(256, 512, 1 << 24, (1 << 25) + 4, 64)) == N.DIT_ERR_INVALID
+    assert call(temb=None) == N.DIT_ERR_INVALID
+    assert call(x_=x + 2) == N.DIT_ERR_INVALID                 # misaligned input
+    assert call(v_=x + 1024) == N.DIT_ERR_INVALID              # v overlaps x
+    assert call(ws_=v + 4096) == N.DIT_ERR_INVALID             # workspace overlaps v
+    assert call(layout=N.make_layout(600, 96, 640)) == N.DIT_ERR_INVALID
+    assert "out_channels" in (call(head=N.DitHeadWeights(256, 512, 1 << 24, None, 12)) and N.last_error())
+    # an empty sequence validates and enqueues nothing
+    assert call(layout=N.make_layout(0, 0, 0), nbytes=256) == N.DIT_OK
