@@ -24,12 +24,17 @@
 //    run the masking code.
 //  * Softmax shift: q and k of the DiT block come out of the per-head Q/K RMSNorm, so every
 //    logit is bounded by max|gq| max|gk| sqrt(Dh) (a normalised head vector has norm below
-//    sqrt(Dh)). When the caller passes the gains and that bound, in log2 units, is at most 60,
-//    the bound replaces the running row maximum: probabilities stay in [2^-120, 1], the
-//    per-tile max reduction, cross-lane exchange and rescale disappear, and the row sum is
-//    taken from the bf16 probabilities the P V product uses (v_dot2c_f32_bf16). Otherwise the
-//    exact running maximum is kept, with the accumulator rescale run only on tiles where some
-//    row's maximum grew.
+//    sqrt(Dh)). When the caller passes the gains and that bound B, in log2 units, is small, no
+//    running row maximum is needed: for 30 < B <= 60 the probabilities are exp2(s c - B), within
+//    [2^-121, 1]; for B <= 30 no shift is needed at all (softmax is scale invariant): the factor
+//    c = log2(e)/sqrt(Dh) is folded into the Q fragments once per wave, so the score MFMAs yield
+//    log2-unit logits and a probability is a bare exp2 of the score, within [2^-31, 2^31]. The
+//    extra bf16 rounding of q c moves a logit by under 0.005 in log2 units at such bounds (it
+//    grows with the logits, which is why larger bounds keep c in fp32). Either way the per-tile
+//    max reduction, cross-lane exchange and rescale disappear, and the row sum is taken from the
+//    bf16 probabilities the P V product uses (v_dot2c_f32_bf16). Otherwise the exact running
+//    maximum is kept, with the accumulator rescale run only on tiles where some row's maximum
+//    grew.
 //  * Valid-only mode bounds the key sweep by the request's valid length and query tiles that
 //    lie wholly in the tail only write zeros. Fixed-valid mode sweeps the whole padded
 //    length with a key mask. A fully masked tile leaves the running max, the sum and the
@@ -156,6 +161,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   }
 
   const int my_q = q0 + wave * 32 + l32;
+  const float c = a.scale_log2;
   bf16x8 qf[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s) {
@@ -237,12 +243,12 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int e = 0; e < 16; ++e) oacc[t][e] = 0.0f;
   float m_run = -INFINITY;
   float l_run = 0.0f;
-  const float c = a.scale_log2;
 
   // Logit bound from the Q/K RMSNorm gains: a normalised head vector has norm below sqrt(Dh),
-  // so |q.k| < max|gq| max|gk| Dh; the factor 1 + 2^-6 covers the bf16 rounding of q and k.
-  // In log2 units (times c) a bound up to 60 keeps every probability exp2(s c - bound) within
-  // [2^-120, 1], normal in fp32 and bf16: the bound then serves as the row maximum.
+  // so |q.k| < max|gq| max|gk| Dh; the factor 1 + 2^-6 covers the bf16 roundings of q, k and
+  // q c. In log2 units (times c): up to 30, every probability exp2(s c) lies in [2^-31, 2^31]
+  // (P V sums stay far from fp32 overflow); up to 60, exp2(s c - bound) lies in [2^-121, 1].
+  // Both are normal in fp32 and bf16, and no running maximum is needed.
   float bound = INFINITY;
   if (a.q_gain != nullptr && a.k_gain != nullptr) {
     float gq = 0.0f, gk = 0.0f;
@@ -258,15 +264,27 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     bound = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
         int, gq * gk * (float)DH * c * (1.0f + 1.0f / 64.0f))));
   }
-  const bool fixed_max = bound <= 60.0f;  // false for an infinite or NaN bound
+  // 2: no shift, 1: shift by the bound, 0: online maximum (also for an infinite or NaN bound)
+  const int shift_mode = bound <= 30.0f ? 2 : (bound <= 60.0f ? 1 : 0);
+  if (shift_mode == 2) {
+    // fold c into the Q fragments: the score MFMAs then yield logits in log2 units
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      bf16x8 scaled;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) scaled[e] = (__bf16)((float)qf[s][e] * c);
+      qf[s] = scaled;
+    }
+  }
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   const int key_end = a.fixed_valid ? L : V;
   const int nkt = (key_end + kKB - 1) / kKB;
   const int n_full = V / kKB;  // tiles whose 64 keys are all valid
 
-  auto tile = [&](auto fixed_c, auto masked_c, auto buf_c, int kt) __attribute__((always_inline)) {
-    constexpr bool FIXED = decltype(fixed_c)::value;
+  auto tile = [&](auto mode_c, auto masked_c, auto buf_c, int kt) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr bool FIXED = MODE != 0;
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr int BUF = decltype(buf_c)::value;
     const bool more = kt + 1 < nkt;
@@ -317,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         }
     }
 
-    // ---- softmax in base 2 with the scale folded into c ----
+    // ---- softmax in base 2 (mode 2: the scores are already in log2 units) ----
     float mc;
     if (FIXED) {
       mc = bound;
@@ -348,7 +366,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][e], c, -mc));
+        const float p = (MODE == 2) ? __builtin_amdgcn_exp2f(sacc[h2][e])
+                                    : __builtin_amdgcn_exp2f(fmaf(sacc[h2][e], c, -mc));
         sacc[h2][e] = p;
         if (!FIXED) psum += p;
       }
@@ -386,26 +405,28 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     __syncthreads();
   };
 
-  auto sweep = [&](auto fixed_c) __attribute__((always_inline)) {
+  auto sweep = [&](auto mode_c) __attribute__((always_inline)) {
     int kt = 0;
     for (; kt + 2 <= n_full; kt += 2) {
-      tile(fixed_c, std::false_type{}, std::integral_constant<int, 0>{}, kt);
-      tile(fixed_c, std::false_type{}, std::integral_constant<int, 1>{}, kt + 1);
+      tile(mode_c, std::false_type{}, std::integral_constant<int, 0>{}, kt);
+      tile(mode_c, std::false_type{}, std::integral_constant<int, 1>{}, kt + 1);
     }
     for (; kt < nkt; ++kt) {
       if (kt & 1)
-        tile(fixed_c, std::true_type{}, std::integral_constant<int, 1>{}, kt);
+        tile(mode_c, std::true_type{}, std::integral_constant<int, 1>{}, kt);
       else
-        tile(fixed_c, std::true_type{}, std::integral_constant<int, 0>{}, kt);
+        tile(mode_c, std::true_type{}, std::integral_constant<int, 0>{}, kt);
     }
   };
   load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (fixed_max)
-    sweep(std::true_type{});
+  if (shift_mode == 2)
+    sweep(std::integral_constant<int, 2>{});
+  else if (shift_mode == 1)
+    sweep(std::integral_constant<int, 1>{});
   else
-    sweep(std::false_type{});
+    sweep(std::integral_constant<int, 0>{});
 
   // ---- normalise and store: element (j, i) of oacc[t] is d = 32 t + 8 j + 4 hh + i ----
   const float l_tot = pair_sum(l_run);

@@ -126,10 +126,11 @@ def test_attention_ragged_batch_full_size(N):
 @pytest.mark.parametrize("head_dim,gain", [(64, 1.0), (128, 1.0), (128, 1.9), (128, 6.0)])
 def test_attention_with_qk_norm_gains(N, head_dim, gain):
     """q and k that came out of the per-head Q/K RMSNorm with gains gq, gk have logits bounded by
-    max|gq| max|gk| sqrt(Dh). Given the gains, the kernel uses that bound in place of the running
-    row maximum when it is small enough (gain 1 and 1.9) and keeps the online maximum otherwise
-    (gain 6). Every case matches the oracle; fixed-valid and valid-only still agree bit for bit,
-    and garbage in the tail rows still leaves the outputs bitwise unchanged."""
+    max|gq| max|gk| sqrt(Dh). Given the gains, the kernel needs no running row maximum when that
+    bound is small: gain 1 (bound 11.7 or 16.6 in log2 units) takes the probabilities unshifted,
+    gain 1.9 (bound 59.9) shifts them by the bound, and gain 6 keeps the online maximum. Every
+    case matches the oracle; fixed-valid and valid-only still agree bit for bit, and garbage in
+    the tail rows still leaves the outputs bitwise unchanged."""
     import oracle as O
     from audio_video_diffusion_dit_amd.inputs import attention_case, bf16_bits, bf16_to_f32
     valid = (1, 77, 300, 513)

@@ -170,15 +170,18 @@ def test_block_h3_sampled_rows(env):
     assert_close(got[rows], ref, "block_h3 sampled rows")
 
 
-@pytest.mark.parametrize("name,gain,path", [("block_small", -2.0, "bound"),
+@pytest.mark.parametrize("name,gain,path", [("block_small", 1.2, "shift-free"),
+                                            ("block_odd", 1.3, "shift-free"),
+                                            ("block_small", -2.0, "bound shift"),
                                             ("block_small", 3.0, "online"),
-                                            ("block_odd", 1.8, "bound"),
+                                            ("block_odd", 1.8, "bound shift"),
                                             ("block_odd", 4.0, "online")])
 def test_block_attention_softmax_paths(env, name, gain, path):
-    """The Q/K RMSNorm gains bound every attention logit by max|gq| max|gk| sqrt(Dh); when that
-    bound (in log2 units, with a 1 + 2^-6 margin) is at most 60 the kernel uses it in place of the
-    running row maximum, otherwise it keeps the online maximum. Both paths match the oracle, per
-    kernel and end to end, with gains that vary across the head dimension and change sign."""
+    """The Q/K RMSNorm gains bound every attention logit by max|gq| max|gk| sqrt(Dh). With that
+    bound B in log2 units (1 + 2^-6 margin) the kernel takes the probabilities as exp2(s) without
+    any shift for B <= 30, as exp2(s - B) for B <= 60, and keeps the online maximum otherwise.
+    Every path matches the oracle, per kernel and end to end, with gains that vary across the
+    head dimension and change sign."""
     import oracle as O
     N, dev = env
     case = _case(name, seed=3)
@@ -190,7 +193,8 @@ def test_block_attention_softmax_paths(env, name, gain, path):
                                 k_g=(gain * ramp[::-1] * sign).astype(np.float32))
     case = dataclasses.replace(case, blocks=[blk_p])
     bound = gain * gain * Dh * (np.log2(np.e) / np.sqrt(Dh)) * (1 + 2 ** -6)
-    assert (bound <= 60) == (path == "bound"), bound
+    want = "shift-free" if bound <= 30 else ("bound shift" if bound <= 60 else "online")
+    assert want == path, bound
     say(f"block {name}: gains up to |{gain}|, logit bound {bound:.1f} (log2 units) -> {path} path")
     out, ws, m = _gpu_block(env, case)
     got = dev.bf16_values_of(out).astype(np.float64)
