@@ -58,6 +58,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kQB = 128;                    // queries per workgroup
 constexpr int kKB = 64;                     // keys per tile
 constexpr int kKPF = 4;                     // K fragments read ahead in the score phase
+constexpr int kVPF = 4;                     // V fragments read ahead in the P V phase
 constexpr int32_t kAttnRsrcWord3 = 0x00020000;
 
 // 16-byte-chunk XOR swizzle of a K row: 16 consecutive rows read at one logical chunk hit
@@ -418,15 +419,199 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         tile(mode_c, std::true_type{}, std::integral_constant<int, 0>{}, kt);
     }
   };
-  load_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (shift_mode == 2)
-    sweep(std::integral_constant<int, 2>{});
-  else if (shift_mode == 1)
-    sweep(std::integral_constant<int, 1>{});
-  else
-    sweep(std::integral_constant<int, 0>{});
+  // ---- shift-free path, software pipelined inside the wave: iteration j issues the score MFMAs
+  // of key tile j in the same instruction stream as the softmax and P V product of tile j - 1,
+  // laid out slot by slot so that every MFMA has two VALU operations beside it. K and V are
+  // staged one tile apart: while iteration j runs, K(j + 1) and V(j) are in flight into the
+  // halves of the double buffer that iteration j - 1 finished reading (K(t) and V(t) live in
+  // buffer t & 1). ----
+  auto load_k = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t g = (uint32_t)kt * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t ok = (DH == 128) ? goff_k[0] + i * gstep : goff_k[i % GK];
+      dma_b128(lds0 + buf * BUFB + i * 4096, g + ok, rs_k);
+    }
+  };
+  auto load_v = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t g = (uint32_t)kt * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t ov = (DH == 128) ? goff_v[0] + i * gstep : goff_v[i % GK];
+      dma_b128(lds0 + buf * BUFB + VOFF + i * 4096, g + ov, rs_v);
+    }
+  };
+  constexpr int NS = 2 * QS;            // score MFMAs per tile
+  constexpr int NP = 4 * DT;            // P V MFMAs per tile
+  // 64 VALU operations per tile (32 exps, 16 packs, 16 row-sum dots): 4 before the first slot,
+  // the rest spread evenly over the NS + NP MFMA slots
+  constexpr int kOpsPerSlot = (60 + NS + NP - 1) / (NS + NP);
+  // every pack (op 3p + 2 of pair p) runs in an earlier slot than the P V MFMA that reads it
+  // (slot NS + DT (p / 4))
+  static_assert([] {
+    for (int p = 0; p < 16; ++p) {
+      const int op = 3 * p + 2;
+      const int slot = op < 4 ? -1 : (op - 4) / ((60 + 2 * (DH / 16) + 4 * (DH / 32) - 1) /
+                                                 (2 * (DH / 16) + 4 * (DH / 32)));
+      if (slot >= 2 * (DH / 16) + (DH / 32) * (p / 4)) return false;
+    }
+    return true;
+  }(), "softmax packs must precede their P V MFMAs");
+  auto kread = [&](int kb, int i) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+                                          lds + kb * BUFB + kaddr_of(i / QS, i % QS)));
+  };
+  // K fragment of score MFMA i of the pipelined path: the two 32-key halves alternate (key half
+  // i & 1, k-step i >> 1), so consecutive MFMAs accumulate into different registers
+  auto kread2 = [&](int kb, int i) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+                                          lds + kb * BUFB + kaddr_of(i & 1, i >> 1)));
+  };
+  auto vread = [&](int vb, int m) __attribute__((always_inline)) {
+    const int ps = m / DT, t = m % DT;
+    lds_char* base = lds + vb * BUFB + vaddr[t] + (16 * ps) * NC * 16;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(base + 8 * NC * 16));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // the first tile's scores and the last tile's P V run on their own, without the slot layout
+  auto s_only = [&](int kb, f32x16 (&sn)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sn[0][e] = 0.0f; sn[1][e] = 0.0f; }
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      sn[i / QS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, i), qf[i % QS], sn[i / QS], 0, 0, 0);
+  };
+  auto pv_only = [&](int vb, f32x16 (&sp)[2]) __attribute__((always_inline)) {
+    uint32_t pk[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const float e0 = __builtin_amdgcn_exp2f(sp[p / 8][(2 * p) % 16]);
+      const float e1 = __builtin_amdgcn_exp2f(sp[p / 8][(2 * p + 1) % 16]);
+      pk[p] = pack_bf16x2(e0, e1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[p]), ones2, l_run, false);
+    }
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int ps = m / DT;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * ps], pk[4 * ps + 1], pk[4 * ps + 2], pk[4 * ps + 3]});
+      oacc[m % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, m), pf, oacc[m % DT], 0, 0, 0);
+    }
+  };
+  // One pipelined iteration: scores of the K tile in buffer kb into sn, and softmax + P V of sp
+  // with the V tile in buffer kb ^ 1, laid out slot by slot: slot k holds MFMA k (score MFMAs
+  // first, then P V), the LDS reads for later slots and two VALU operations of the softmax.
+  auto pipe = [&](auto kb_c, f32x16 (&sn)[2], f32x16 (&sp)[2]) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kb_c)::value;
+    constexpr int vb = kb ^ 1;
+    uint32_t pk[16];
+    bf16x8 kr[kKPF];
+    bf16x8 vr[kVPF];
+    // VALU operation n of the iteration (0..63): exps e0..e31 (element idx of sp), packs of pairs,
+    // row-sum dots; ordered so every pack is ready before its P V MFMA.
+    float ex[32];
+    // ops 0..47: exp, exp, pack for pairs 0..15 (pack of pair p at op 3p + 2, slot 3p/2 - 1 at
+    // the latest, before the P V MFMA of its key group at slot 16 + 4 (p / 4)); ops 48..63: the
+    // row-sum dots, which no MFMA waits for
+    auto valu = [&](int n) __attribute__((always_inline)) {
+      if (n < 48) {
+        const int pair = n / 3, r = n % 3;
+        if (r == 0) ex[2 * pair] = __builtin_amdgcn_exp2f(sp[(2 * pair) / 16][(2 * pair) % 16]);
+        else if (r == 1) ex[2 * pair + 1] = __builtin_amdgcn_exp2f(sp[(2 * pair + 1) / 16][(2 * pair + 1) % 16]);
+        else pk[pair] = pack_bf16x2(ex[2 * pair], ex[2 * pair + 1]);
+      } else {
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[n - 48]), ones2, l_run, false);
+      }
+    };
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sn[0][e] = 0.0f; sn[1][e] = 0.0f; }
+#pragma unroll
+    for (int i = 0; i < kKPF; ++i) kr[i] = kread2(kb, i);
+    valu(0); valu(1); valu(2); valu(3);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NS + NP; ++k) {
+      if (k < NS) {
+        const bf16x8 kf = kr[k % kKPF];
+        if (k + kKPF < NS) kr[k % kKPF] = kread2(kb, k + kKPF);
+        sn[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k >> 1], sn[k & 1], 0, 0, 0);
+        if (k >= NS - kVPF) vr[k - (NS - kVPF)] = vread(vb, k - (NS - kVPF));
+      } else {
+        const int m = k - NS;
+        const int ps = m / DT;
+        const bf16x8 vf = vr[m % kVPF];
+        if (m + kVPF < NP) vr[m % kVPF] = vread(vb, m + kVPF);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * ps], pk[4 * ps + 1], pk[4 * ps + 2], pk[4 * ps + 3]});
+        oacc[m % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[m % DT], 0, 0, 0);
+      }
+      // two VALU operations per slot (ops 4..63 over slots 0..29)
+#pragma unroll
+      for (int r = 0; r < kOpsPerSlot; ++r)
+        if (4 + kOpsPerSlot * k + r < 64) valu(4 + kOpsPerSlot * k + r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto mask_tile = [&](f32x16 (&sn)[2], int kt) __attribute__((always_inline)) {
+    const int kv0 = kt * kKB;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kv0 + h2 * 32 + (e >> 2) * 8 + 4 * hh + (e & 3);
+        if (key >= V) sn[h2][e] = -INFINITY;
+      }
+  };
+  auto step = [&](auto kb_c, auto masked_c, f32x16 (&sn)[2], f32x16 (&sp)[2], int j)
+      __attribute__((always_inline)) {
+    constexpr int KB = decltype(kb_c)::value;
+    if (j + 1 < nkt) load_k(j + 1, KB ^ 1);
+    load_v(j, KB);
+    pipe(kb_c, sn, sp);
+    if constexpr (decltype(masked_c)::value) mask_tile(sn, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  auto sweep_pipelined = [&]() __attribute__((always_inline)) {
+    f32x16 sA[2], sB[2];
+    load_k(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (nkt > 1) load_k(1, 1);
+    load_v(0, 0);
+    s_only(0, sA);
+    if (0 >= n_full) mask_tile(sA, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // steps j < n_full compute unmasked score tiles; the rest (at most the last partial tile,
+    // plus the tail tiles in fixed-valid mode) mask theirs
+    int j = 1;
+    for (; j + 2 <= nkt && j + 1 < n_full; j += 2) {
+      step(std::integral_constant<int, 1>{}, std::false_type{}, sB, sA, j);
+      step(std::integral_constant<int, 0>{}, std::false_type{}, sA, sB, j + 1);
+    }
+    for (; j + 2 <= nkt; j += 2) {
+      step(std::integral_constant<int, 1>{}, std::true_type{}, sB, sA, j);
+      step(std::integral_constant<int, 0>{}, std::true_type{}, sA, sB, j + 1);
+    }
+    if (j < nkt) {
+      step(std::integral_constant<int, 1>{}, std::true_type{}, sB, sA, j);
+      pv_only(1, sB);
+    } else {
+      pv_only(0, sA);
+    }
+  };
+
+  if (shift_mode == 2) {
+    sweep_pipelined();
+  } else {
+    load_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (shift_mode == 1)
+      sweep(std::integral_constant<int, 1>{});
+    else
+      sweep(std::integral_constant<int, 0>{});
+  }
 
   // ---- normalise and store: element (j, i) of oacc[t] is d = 32 t + 8 j + 4 hh + i ----
   const float l_tot = pair_sum(l_run);
