@@ -139,7 +139,8 @@ struct AttnArgs {
   float scale_log2;     // log2(e) / sqrt(head_dim)
   // Optional per-dimension gains [head_dim] of the Q/K RMSNorm that produced q and k (both or
   // neither). With them the kernel bounds every logit and, when the bound is small enough,
-  // replaces the running row maximum by that bound (softmax is shift invariant).
+  // needs no running row maximum: it shifts by the bound, or not at all (softmax is shift and
+  // scale invariant).
   const float* q_gain;
   const float* k_gain;
   int32_t valid[ATTN_MAX_BATCH];

@@ -279,9 +279,10 @@ int dit_velocity_head_f32(const dit_dims* dims, const dit_layout* layout,
  * valid_lens: host int32 [batch], each in [0, seq_pad]; batch <= 64; head_dim 64 or 128.
  * q_gain, k_gain: dev fp32 [head_dim] or both NULL. When given, q and k must be outputs of the
  * per-head Q/K RMSNorm with these gains ([P3] "Changes Made": fused Q/K RMSNorm), which bounds
- * every logit by max|q_gain| max|k_gain| sqrt(head_dim); the kernel then may use that bound in
- * place of the running row maximum (same result up to rounding). Passing gains for q, k that
- * did not come out of such a norm is undefined. */
+ * every logit by max|q_gain| max|k_gain| sqrt(head_dim); when that bound is small the kernel
+ * needs no running row maximum (it shifts by the bound, or for bounds up to 30 in log2 units
+ * not at all; same result up to rounding). Passing gains for q, k that did not come out of
+ * such a norm is undefined. */
 int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           uint16_t* o, int32_t batch, int32_t seq_pad, int32_t heads,
                           int32_t head_dim, int64_t batch_stride, int64_t row_stride,
