@@ -108,6 +108,38 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
     const bool valid = ri.valid;
     const int mod = ri.mod;
     constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
+    // Gated epilogues: every load of this token row (residual and gate values) is issued before
+    // the row's first store, so they share one memory round trip. The compiler cannot prove that
+    // the output stores do not alias them and would otherwise keep each load group behind the
+    // previous store. Feature offsets past N are clamped to a valid address (the values are
+    // then discarded).
+    float rv[OUT_T][4][4];
+    float gv[OUT_T][4][4];
+    if constexpr (GATED) {
+#pragma unroll
+      for (int f = 0; f < OUT_T; ++f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int fb0 = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
+          const int fb = fb0 < a.N ? fb0 : a.N - 4;
+          if constexpr (EPI == EPI_GATED_TO_F32) {
+            const u32x2 rr = *reinterpret_cast<const u32x2*>(
+                static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fb);
+            rv[f][j][0] = bf_lo(rr.x); rv[f][j][1] = bf_hi(rr.x);
+            rv[f][j][2] = bf_lo(rr.y); rv[f][j][3] = bf_hi(rr.y);
+          } else {
+            const float4 rr = *reinterpret_cast<const float4*>(
+                static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
+            rv[f][j][0] = rr.x; rv[f][j][1] = rr.y; rv[f][j][2] = rr.z; rv[f][j][3] = rr.w;
+          }
+          const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
+          const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
+          const float4 gt = *reinterpret_cast<const float4*>(a.temb + ri.req * a.temb_stride + goff);
+          gv[f][j][0] = ga.x + gt.x; gv[f][j][1] = ga.y + gt.y;
+          gv[f][j][2] = ga.z + gt.z; gv[f][j][3] = ga.w + gt.w;
+        }
+      }
+    }
 #pragma unroll
     for (int f = 0; f < OUT_T; ++f) {
 #pragma unroll
@@ -121,23 +153,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
             for (int i = 0; i < 4; ++i)
               o[i] = silu_mul(acc[2 * f][t][4 * j + i], acc[2 * f + 1][t][4 * j + i]);
           } else if constexpr (GATED) {
-            float r[4];
-            if constexpr (EPI == EPI_GATED_TO_F32) {
-              const u32x2 rr = *reinterpret_cast<const u32x2*>(
-                  static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fb);
-              r[0] = bf_lo(rr.x); r[1] = bf_hi(rr.x); r[2] = bf_lo(rr.y); r[3] = bf_hi(rr.y);
-            } else {
-              const float4 rr = *reinterpret_cast<const float4*>(
-                  static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
-              r[0] = rr.x; r[1] = rr.y; r[2] = rr.z; r[3] = rr.w;
-            }
-            const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
-            const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
-            const float4 gt = *reinterpret_cast<const float4*>(a.temb + ri.req * a.temb_stride + goff);
-            o[0] = fmaf(ga.x + gt.x, acc[f][t][4 * j + 0], r[0]);
-            o[1] = fmaf(ga.y + gt.y, acc[f][t][4 * j + 1], r[1]);
-            o[2] = fmaf(ga.z + gt.z, acc[f][t][4 * j + 2], r[2]);
-            o[3] = fmaf(ga.w + gt.w, acc[f][t][4 * j + 3], r[3]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = fmaf(gv[f][j][i], acc[f][t][4 * j + i], rv[f][j][i]);
           } else if constexpr (EPI == EPI_BIAS_TO_F32) {
             float4 b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (a.bias) b = *reinterpret_cast<const float4*>(a.bias + (int64_t)mod * a.N + fb);
