@@ -18,7 +18,7 @@ def env():
     return _native, device
 
 
-def _run(env, wl_dims, reqs, seq_pad, seed):
+def _run(env, wl_dims, reqs, seq_pad, seed, attn_mode=0):
     """reqs: list of (n_video, n_audio, positions or None). Returns batched and single outputs."""
     import torch
     import oracle as O
@@ -42,7 +42,7 @@ def _run(env, wl_dims, reqs, seq_pad, seed):
     out.view(torch.int16).fill_(0x7FC0)
     nbytes, _ = N.dit_workspace_size_batched(dims, lays)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    N.dit_block_forward_batched(dims, lays, blk.weights, dt, dx, out, 0, ws)
+    N.dit_block_forward_batched(dims, lays, blk.weights, dt, dx, out, attn_mode, ws)
     torch.cuda.synchronize()
     got = dev.bf16_bits_of(out)
     singles = []
@@ -113,3 +113,14 @@ def test_batched_block_ragged_full_size(env):
         ref = O.block_forward(xs, oracle_block(blk_p), temb[b], oracle_dims(wl), O.Layout(nv, na, L),
                               rows=rows)
         assert_close(I.bf16_to_f32(got[b * L + rows]), ref, f"request {b} sampled rows vs oracle")
+
+
+def test_batched_fixed_valid_equals_valid_only(env):
+    """Fixed-valid attention inside the batched block (every key tile of each request swept with
+    a mask) gives the valid-only result bit for bit."""
+    N, _ = env
+    reqs = [(400, 100, None), (0, 0, None), (700, 60, None)]
+    say("batched block: fixed-valid vs valid-only, 3 requests x 768 rows")
+    *_, vo, _ = _run(env, (256, 4, 64, 683), reqs, 768, seed=16, attn_mode=N.DIT_ATTN_VALID_ONLY)
+    *_, fv, _ = _run(env, (256, 4, 64, 683), reqs, 768, seed=16, attn_mode=N.DIT_ATTN_FIXED_VALID)
+    assert np.array_equal(vo, fv)
