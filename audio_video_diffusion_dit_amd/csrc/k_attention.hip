@@ -453,9 +453,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
   static_assert([] {
     for (int p = 0; p < 16; ++p) {
       const int op = 3 * p + 2;
-      const int slot = op < 4 ? -1 : (op - 4) / ((60 + 2 * (DH / 16) + 4 * (DH / 32) - 1) /
-                                                 (2 * (DH / 16) + 4 * (DH / 32)));
-      if (slot >= 2 * (DH / 16) + (DH / 32) * (p / 4)) return false;
+      const int slot = op < 4 ? -1 : (op - 4) / kOpsPerSlot;
+      if (slot >= NS + DT * (p / 4)) return false;
     }
     return true;
   }(), "softmax packs must precede their P V MFMAs");
