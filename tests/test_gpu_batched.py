@@ -124,3 +124,22 @@ def test_batched_fixed_valid_equals_valid_only(env):
     *_, vo, _ = _run(env, (256, 4, 64, 683), reqs, 768, seed=16, attn_mode=N.DIT_ATTN_VALID_ONLY)
     *_, fv, _ = _run(env, (256, 4, 64, 683), reqs, 768, seed=16, attn_mode=N.DIT_ATTN_FIXED_VALID)
     assert np.array_equal(vo, fv)
+
+
+def test_batched_maximum_batch(env):
+    """The largest batch the entry point takes: 64 requests of 256 rows at hidden 256, valid
+    lengths drawn in [0, 256] (video and audio split at random); every request equals its own
+    single-request call bit for bit."""
+    rng = np.random.default_rng(17)
+    reqs = []
+    for _ in range(64):
+        n = int(rng.integers(0, 257))
+        nv = int(rng.integers(0, n + 1))
+        reqs.append((nv, n - nv, None))
+    reqs[0] = (200, 56, None)        # one full request; make_block takes its layout
+    say(f"batched block: 64 requests x 256 rows, valid {min(a + b for a, b, _ in reqs)}.."
+        f"{max(a + b for a, b, _ in reqs)}")
+    _, _, _, _, got, singles = _run(env, (256, 4, 64, 683), reqs, 256, seed=18)
+    for b, (nv, na, _) in enumerate(reqs):
+        assert np.array_equal(got[b * 256:(b + 1) * 256], singles[b]), f"request {b} differs"
+        assert np.all(got[b * 256 + nv + na:(b + 1) * 256] == 0)
