@@ -100,7 +100,7 @@ def _load():
     lib.dit_block_forward_f32.restype = c_int32
     lib.dit_block_forward_f32.argtypes = lib.dit_block_forward.argtypes
     lib.dit_head_workspace_size.restype = c_size_t
-    lib.dit_head_workspace_size.argtypes = [POINTER(DitDims), POINTER(DitLayout)]
+    lib.dit_head_workspace_size.argtypes = [POINTER(DitDims), POINTER(DitLayout), c_int32]
     lib.dit_velocity_head.restype = c_int32
     lib.dit_velocity_head.argtypes = [POINTER(DitDims), POINTER(DitLayout), POINTER(DitHeadWeights),
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -248,8 +248,8 @@ def dit_block_forward_f32(dims, layout, weights: DitBlockWeights, temb, x_in, x_
                                      ws_bytes, _stream(stream)), "dit_block_forward_f32")
 
 
-def dit_head_workspace_size(dims, layout) -> int:
-    n = lib.dit_head_workspace_size(ctypes.byref(dims), ctypes.byref(layout))
+def dit_head_workspace_size(dims, layout, out_channels) -> int:
+    n = lib.dit_head_workspace_size(ctypes.byref(dims), ctypes.byref(layout), out_channels)
     if n == 0:
         raise AvditError(DIT_ERR_INVALID, "dit_head_workspace_size", last_error())
     return n

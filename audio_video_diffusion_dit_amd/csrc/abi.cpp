@@ -638,9 +638,24 @@ int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* 
 namespace {
 
 constexpr int32_t kMaxOutChannels = 1 << 16;
+// A projection to few channels carries little matrix work per k-tile, so one workgroup's walk
+// over the reduction is a chain of load latencies: for C <= 256 the reduction is split four
+// ways (fp32 partials in the workspace, summed in order by one reduction pass).
+constexpr int kHeadSplits = 4;
 
-size_t head_ws_bytes(const dit_dims* d, const dit_layout* l) {
-  const size_t n = align_up((size_t)l->seq_pad * d->hidden * 2);
+int head_splits(const dit_dims* d, int32_t C) {
+  return (C <= 256 && d->hidden % (kHeadSplits * 64) == 0) ? kHeadSplits : 1;
+}
+
+// workspace: h [seq_pad, D] bf16, then (split reduction) the partials [splits, seq_pad, C] fp32
+size_t head_h_bytes(const dit_dims* d, const dit_layout* l) {
+  return align_up((size_t)l->seq_pad * d->hidden * 2);
+}
+
+size_t head_ws_bytes(const dit_dims* d, const dit_layout* l, int32_t C) {
+  size_t n = head_h_bytes(d, l);
+  const int S = head_splits(d, C);
+  if (S > 1) n += align_up((size_t)S * l->seq_pad * C * 4);
   return n < kAlign ? kAlign : n;
 }
 
@@ -663,7 +678,7 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
   if (!temb || !x || !v) return fail(DIT_ERR_INVALID, "temb, x and v must be non-null");
   if ((((uintptr_t)x) & 15) || (((uintptr_t)v) & 15))
     return fail(DIT_ERR_INVALID, "x and v must be 16-byte aligned");
-  const size_t need = head_ws_bytes(dims, layout);
+  const size_t need = head_ws_bytes(dims, layout, C);
   if ((st = check_ws(ws, ws_bytes, need)) != DIT_OK) return st;
   const int32_t D = dims->hidden, L = layout->seq_pad;
   const int32_t nv = layout->n_video, V = layout->n_video + layout->n_audio;
@@ -683,17 +698,29 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
   if ((st = device_status(launch_norm_mod(n, s), "final norm+modulation")) != DIT_OK) return st;
 
   // One launch per modality over its own rows; the audio launch also writes the zero tail.
-  // Row modality inside a launch comes from its RowLayout, which selects the bias row.
+  // Row modality inside a launch comes from its RowLayout, which selects the bias row. With a
+  // split reduction the launches write fp32 partials and one pass adds them and the bias.
+  const int S = head_splits(dims, C);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + head_h_bytes(dims, layout));
+  const int64_t split_stride = (int64_t)L * C;
   for (int m = 0; m < 2; ++m) {
     const int32_t r0 = m == 0 ? 0 : nv;
     const int32_t rows = m == 0 ? nv : L - nv;
     if (rows <= 0) continue;
     GemmArgs g{};
-    g.A = h + (size_t)r0 * D; g.W = hw->w_out + (size_t)m * C * D; g.C = v + (size_t)r0 * C;
+    g.A = h + (size_t)r0 * D; g.W = hw->w_out + (size_t)m * C * D;
+    g.C = (S > 1 ? partials : v) + (size_t)r0 * C;
     g.lda = D; g.ldw = D; g.ldc = C; g.N = C; g.K = D;
     g.rows = m == 0 ? RowLayout{nv, nv, nv} : RowLayout{0, V - nv, L - nv};
-    g.epilogue = EPI_BIAS_TO_F32; g.bias = hw->bias;
+    g.epilogue = EPI_BIAS_TO_F32; g.bias = S > 1 ? nullptr : hw->bias;
+    g.k_splits = S; g.split_stride = split_stride;
     if ((st = device_status(launch_gemm(g, s), "head projection")) != DIT_OK) return st;
+  }
+  if (S > 1) {
+    SplitReduceArgs r{};
+    r.partials = partials; r.out = v; r.bias = hw->bias; r.rows = RowLayout{nv, V, L};
+    r.C = C; r.splits = S; r.split_stride = split_stride;
+    if ((st = device_status(launch_split_reduce(r, s), "head reduction")) != DIT_OK) return st;
   }
   return DIT_OK;
 }
@@ -702,10 +729,16 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
 
 extern "C" {
 
-size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout) {
+size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout,
+                               int32_t out_channels) {
   g_err.clear();
   if (check_dims(dims) != DIT_OK || check_layout(layout) != DIT_OK) return 0;
-  return head_ws_bytes(dims, layout);
+  if (out_channels <= 0 || (out_channels & 7) != 0 || out_channels > kMaxOutChannels) {
+    fail(DIT_ERR_INVALID, "out_channels %d must be a positive multiple of 8, at most %d",
+         out_channels, kMaxOutChannels);
+    return 0;
+  }
+  return head_ws_bytes(dims, layout, out_channels);
 }
 
 int dit_velocity_head(const dit_dims* dims, const dit_layout* layout,

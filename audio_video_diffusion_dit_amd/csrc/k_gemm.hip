@@ -92,8 +92,8 @@ __device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_
 // 8 j + 4 hh (SwiGLU pairs gate sub-tile 2 f with up sub-tile 2 f + 1). Invalid rows (at or past
 // a request's valid length) are written 0, rows past the last request are not written.
 template <int EPI, int FT, int MT, int TM, int TN>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][MT], int m0, int n0,
-                                           int wm, int wn, int lane) {
+__device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&acc)[FT][MT], int m0,
+                                           int n0, int wm, int wn, int lane) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int rows_total = total_rows(a.rows);
@@ -169,10 +169,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[FT][
           }
         }
         if constexpr (OUT_F32) {
-          float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
+          float* crow = static_cast<float*>(C) + (int64_t)tok * a.ldc;
           *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
         } else {
-          uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
+          uint16_t* crow = static_cast<uint16_t*>(C) + (int64_t)tok * a.ldc;
           if (fb + 4 <= a.N) {
             *reinterpret_cast<u32x2*>(crow + fb) =
                 u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
@@ -212,6 +212,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
 
   int tile_m, tile_n;
   select_tile(tiles_m, tiles_n, tile_m, tile_n);
+  // k split y = blockIdx.y (one split: y = 0, the whole reduction): operands advanced to the
+  // split's k range, fp32 partial output y
+  const int Kp = a.K / a.k_splits;
+  const uint16_t* const gA = a.A + (int64_t)blockIdx.y * Kp;
+  const uint16_t* const gW = a.W + (int64_t)blockIdx.y * Kp;
+  void* const gC = static_cast<float*>(a.C) + (int64_t)blockIdx.y * a.split_stride;
 
   const int m0 = tile_m * BM;
   const int rows_total = total_rows(a.rows);
@@ -229,8 +235,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
   if (rows_have_valid(a.rows, m0)) {
     const int ck = tid & 7;
     const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
-    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A, (uint32_t)((int64_t)rows_total * a.lda * 2));
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(gW, (uint32_t)((int64_t)w_rows * a.ldw * 2));
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(gA, (uint32_t)((int64_t)rows_total * a.lda * 2));
     // byte offset of each staged row (kOob when the row is masked)
     uint32_t src_off[PT];
     int src_row[PT];
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
         src_off[i] = src_ok[i] ? (uint32_t)((int64_t)tok * a.lda * 2) : kOob;
       }
     }
-    const int nk = (a.K + kBK - 1) / kBK;
+    const int nk = (Kp + kBK - 1) / kBK;
     u32x4 stage[PT];
     auto load_stage = [&](int kt) {
       const int k = kt * kBK + ck * 8;
@@ -267,12 +273,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
         // staging step i covers rows RPI*i .. RPI*i + RPI - 1: all weight rows or all token rows
         const bool w_step = i < BN / RPI;
         if (ALIGNED) {
-          const uint32_t off = (k < a.K) ? src_off[i] + (uint32_t)(k * 2) : kOob;
+          const uint32_t off = (k < Kp) ? src_off[i] + (uint32_t)(k * 2) : kOob;
           stage[i] = w_step ? __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0)
                             : __builtin_amdgcn_raw_buffer_load_b128(rs_a, off, 0, 0);
         } else {
-          stage[i] = w_step ? load_chunk_slow(a.W, a.ldw, src_row[i], src_ok[i], k, a.K)
-                            : load_chunk_slow(a.A, a.lda, src_row[i], src_ok[i], k, a.K);
+          stage[i] = w_step ? load_chunk_slow(gW, a.ldw, src_row[i], src_ok[i], k, Kp)
+                            : load_chunk_slow(gA, a.lda, src_row[i], src_ok[i], k, Kp);
         }
       }
     };
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
     }
   }
 
-  store_tile<EPI, FT, MT, TM, TN>(a, acc, m0, n0, wm, wn, lane);
+  store_tile<EPI, FT, MT, TM, TN>(a, gC, acc, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -479,7 +485,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
     }
     mfmas((KS - 1) & 1);
   }
-  store_tile<EPI, FT, MT, TM, TN>(a, acc, m0, n0, wm, wn, lane);
+  store_tile<EPI, FT, MT, TM, TN>(a, a.C, acc, m0, n0, wm, wn, lane);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
@@ -489,8 +495,8 @@ static hipError_t gemm_instance(const GemmArgs& a, hipStream_t s) {
   const int tiles_n = (a.N + out_per_tile - 1) / out_per_tile;
   const int nt = tiles_m * tiles_n;
   if (nt == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, ALIGNED>), dim3(nt), dim3(64 * WM * WN), 0, s,
-                     a, tiles_m, tiles_n);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, ALIGNED>), dim3(nt, a.k_splits),
+                     dim3(64 * WM * WN), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -518,6 +524,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.epilogue == EPI_BIAS_TO_F32 &&
       ((a.N & 3) != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 15) != 0))
     return hipErrorInvalidValue;
+  if (a.k_splits != 1) {
+    // split reductions: fp32 partial outputs only, whole k-tiles per split, register-staged path
+    if (a.k_splits < 1 || a.k_splits > 64 || a.epilogue != EPI_BIAS_TO_F32 || a.bias != nullptr ||
+        a.K % (a.k_splits * kBK) != 0 || a.split_stride <= 0)
+      return hipErrorInvalidValue;
+    const bool al = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.W) & 15) == 0);
+    return al ? gemm_instance<128, 128, 2, 2, EPI_BIAS_TO_F32, true>(a, s)
+              : gemm_instance<128, 128, 2, 2, EPI_BIAS_TO_F32, false>(a, s);
+  }
   // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
   const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
   if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)total_rows(a.rows) * a.lda * 2 >= (int64_t)kOob)

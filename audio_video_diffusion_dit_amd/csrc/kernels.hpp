@@ -122,8 +122,26 @@ struct GemmArgs {
   int32_t up_offset;      // EPI_SWIGLU: first up row of W (= F)
   int64_t temb_stride;    // gated epilogues: elements between successive requests' temb tables
   const float* bias = nullptr;  // EPI_BIAS_TO_F32: [2, N] per-modality bias, or null
+  // Split of the reduction (EPI_BIAS_TO_F32 without bias only): workgroup (tile, y) reduces over
+  // k in [y K / k_splits, (y + 1) K / k_splits) and writes its fp32 partial sums to
+  // C + y * split_stride.
+  int32_t k_splits = 1;
+  int64_t split_stride = 0;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// v[row][c] = sum over s of P[s][row][c] (s in order) + bias[mod(row)][c] for valid rows, 0 for
+// the tail: the reduction of a split-K projection. P: splits x [rows, C] fp32, split_stride
+// elements apart; C a multiple of 4.
+struct SplitReduceArgs {
+  const float* partials;
+  float* out;
+  const float* bias;  // [2, C] or null
+  RowLayout rows;
+  int32_t C, splits;
+  int64_t split_stride;
+};
+hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s);
 
 // Flash-style attention over packed requests; element (b, i, h, d) of q/k/v at
 // b * batch_stride + i * row_stride + h * head_dim + d.

@@ -293,7 +293,7 @@ def configs_report(args):
           dev.to_dev_f32(hp.bias)]
     head = N.make_head(*hw, C)
     dims, lay = dev.dims_of(wl), dev.layout_of(wl)
-    ws = torch.empty(N.dit_head_workspace_size(dims, lay), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(N.dit_head_workspace_size(dims, lay, C), dtype=torch.uint8, device="cuda")
     vh = torch.empty((wl.seq_pad, C), dtype=torch.float32, device="cuda")
     ms = gpu_ms(lambda: N.dit_velocity_head(dims, lay, head, th, xh, vh, ws, stream=stream))
     V, D, L = wl.n_valid, wl.hidden, wl.seq_pad

@@ -246,10 +246,12 @@ int denoise_loop_f32(const dit_dims* dims, const dit_layout* layout,
                      int32_t attn_mode, dit_loop_stats* stats, void* ws, size_t ws_bytes,
                      void* stream);
 
-/* Workspace of dit_velocity_head and dit_velocity_head_f32 (the modulated norm, bf16
- * [seq_pad, D]). A block workspace of the same dims and layout is large enough. Returns 0 with
- * dit_last_error() set for invalid dims or layout. */
-size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout);
+/* Workspace of dit_velocity_head and dit_velocity_head_f32 for out_channels output channels:
+ * the modulated norm (bf16 [seq_pad, D]) and, for out_channels <= 256 (the projection's
+ * reduction is then split four ways), fp32 partial sums [4, seq_pad, out_channels]. Returns 0
+ * with dit_last_error() set for invalid dims, layout or out_channels. */
+size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout,
+                               int32_t out_channels);
 
 /* Velocity head ([P2] "Test Result", final AdaLN layer; [P1] section 1): for a valid row l of
  * modality m, h = x_l / sqrt(mean(x_l^2) + norm_eps) * norm_g * (1 + E[m][1]) + E[m][0] with

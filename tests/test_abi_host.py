@@ -246,13 +246,14 @@ def test_denoise_loop_rejects_invalid_arguments(N):
 def test_head_workspace_and_validation(N):
     d = N.make_dims(256, 4, 64, 683)
     lay = N.make_layout(512, 96, 640)
-    need = N.dit_head_workspace_size(d, lay)
-    assert need == 640 * 256 * 2
-    n_blk, _ = N.dit_workspace_size(d, lay, 0)
-    assert n_blk >= need
-    assert N.dit_head_workspace_size(d, N.make_layout(0, 0, 0)) == 256
+    need = N.dit_head_workspace_size(d, lay, 64)
+    assert need == 640 * 256 * 2 + 4 * 640 * 64 * 4          # h, then 4 split partial planes
+    assert N.dit_head_workspace_size(d, lay, 512) == 640 * 256 * 2   # wide heads: no split
+    assert N.dit_head_workspace_size(d, N.make_layout(0, 0, 0), 64) == 256
     with pytest.raises(N.AvditError):
-        N.dit_head_workspace_size(d, N.make_layout(600, 96, 640))
+        N.dit_head_workspace_size(d, N.make_layout(600, 96, 640), 64)
+    with pytest.raises(N.AvditError):
+        N.dit_head_workspace_size(d, lay, 12)
     f = N.lib.dit_velocity_head
     ws, x, v, t = 1 << 30, 1 << 32, 1 << 34, 1 << 20
     good = N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 64)

@@ -46,7 +46,7 @@ def _gpu(env, wl, hp, x, temb, bias=True, f32=False, x_tail=None, ws_fill=None):
     head = N.make_head(g, a, w, b if bias else None, C)
     dims = N.make_dims(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
     lay = N.make_layout(wl.n_video, wl.n_audio, wl.seq_pad)
-    ws = torch.empty(N.dit_head_workspace_size(dims, lay), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(N.dit_head_workspace_size(dims, lay, C), dtype=torch.uint8, device="cuda")
     if ws_fill is not None:
         ws.fill_(ws_fill)
     v = torch.full((wl.seq_pad, C), float("nan"), dtype=torch.float32, device="cuda")
