@@ -21,6 +21,11 @@ pages print, except ``block_forward`` as a whole, whose composition is pinned
 only through its parts and a brute-force scalar re-derivation on a tiny shape
 ("parity unpinned" against the pages: they print no numeric example of a block), and
 ``velocity_head``, pinned by closed forms (one-hot rows, a scale of -1) and scalar loops.
+
+Diagnostics (never the graded reference): ``block_forward_bf16_storage`` and
+``attention_bf16_storage`` are the same functions with the intermediates a bf16
+implementation stores rounded to bf16 where they are stored; pinned bit for bit
+against scalar loops that round each stored element.
 """
 
 from __future__ import annotations
@@ -194,13 +199,17 @@ def rope_neox(t: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
-def attention_valid(q, k, v, n_valid: int) -> np.ndarray:
+def attention_valid(q, k, v, n_valid: int, p_store: Optional[Callable] = None) -> np.ndarray:
     """Softmax attention restricted to the valid prefix; q, k, v [L, H, Dh].
 
     [P1 §2] valid-only attention with zero-tail merge: queries and keys with index
     < n_valid attend to each other bidirectionally (jointly over both
     modalities), with scores q.k / sqrt(Dh); output rows >= n_valid are 0. Rows of
     the inputs at or beyond n_valid are never read.
+
+    p_store (diagnostic only, default none): applied to the unnormalised
+    probabilities before they weight the values and are summed, i.e. the form in
+    which they are stored as the operand of the P.V product.
     """
     q = np.asarray(q, dtype=F64)
     L, H, Dh = q.shape
@@ -213,14 +222,17 @@ def attention_valid(q, k, v, n_valid: int) -> np.ndarray:
     s = (qv @ kv.transpose(0, 2, 1)) / math.sqrt(Dh)               # [H, V, V]
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
+    if p_store is not None:
+        p = p_store(p)
     p = p / p.sum(axis=-1, keepdims=True)
     out[:n_valid] = (p @ vv).transpose(1, 0, 2)
     return out
 
 
-def attention_rows(q_rows, k, v, n_valid: int) -> np.ndarray:
+def attention_rows(q_rows, k, v, n_valid: int, p_store: Optional[Callable] = None) -> np.ndarray:
     """Attention output for a subset of query rows q_rows [R, H, Dh] against the
-    valid keys k[:n_valid], v[:n_valid] (same definition as ``attention_valid``)."""
+    valid keys k[:n_valid], v[:n_valid] (same definition as ``attention_valid``,
+    p_store likewise)."""
     q_rows = np.asarray(q_rows, dtype=F64)
     Dh = q_rows.shape[-1]
     kv = np.asarray(k, dtype=F64)[:n_valid].transpose(1, 0, 2)     # [H, V, Dh]
@@ -229,6 +241,8 @@ def attention_rows(q_rows, k, v, n_valid: int) -> np.ndarray:
     s = (qr @ kv.transpose(0, 2, 1)) / math.sqrt(Dh)
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
+    if p_store is not None:
+        p = p_store(p)
     p = p / p.sum(axis=-1, keepdims=True)
     return (p @ vv).transpose(1, 0, 2)
 
@@ -249,7 +263,8 @@ def swiglu(h, w_gate_up, ffn: int) -> np.ndarray:
 def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
                   positions: Optional[np.ndarray] = None,
                   rows: Optional[np.ndarray] = None,
-                  want_intermediates: bool = False):
+                  want_intermediates: bool = False,
+                  store: Optional[Callable[[str, np.ndarray], np.ndarray]] = None):
     """One joint audio-video DiT block on the packed sequence x [L, D].
 
     Composition (the pre-norm AdaLN DiT block that uses every fused operation the
@@ -264,7 +279,16 @@ def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
       x2  = x1 + E[m,5] * (SwiGLU(h2) Wd^T)
     Tail rows of x2 are 0. With ``rows`` given, only those output rows are
     computed (keys and values still come from every valid row).
+
+    ``store`` (diagnostic only; None for the definition above) is applied to each
+    intermediate where a fused implementation writes it out, under these names:
+    "h" (norm1 output), "qkv" (the q, k and v projections), "qk" (q and k after
+    Q/K norm and RoPE), "p" (the unnormalised attention probabilities as the
+    operand of the P.V product; the softmax denominator sums the stored values),
+    "o" (attention output), "x1" (mid-block residual), "h2" (norm2 output),
+    "act" (SwiGLU output) and "out" (the block output on valid rows).
     """
+    st = store if store is not None else (lambda name, a: a)
     D, H, Dh, F = dims.hidden, dims.heads, dims.head_dim, dims.ffn
     x = np.asarray(x, dtype=F64)
     L = layout.seq_pad
@@ -273,31 +297,34 @@ def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
     pos = row_positions(layout, positions)
     E = modulation_rows(blk["ada"], temb)
 
-    h = norm_modulate(x, blk["norm1_g"], E, mod, SHIFT_MSA, SCALE_MSA, dims.norm_eps)
+    h = st("h", norm_modulate(x, blk["norm1_g"], E, mod, SHIFT_MSA, SCALE_MSA, dims.norm_eps))
     w_qkv = np.asarray(blk["w_qkv"], dtype=F64)
     kv_rows = slice(0, V)
-    k = linear(h[kv_rows], w_qkv[D:2 * D]).reshape(V, H, Dh)
-    v = linear(h[kv_rows], w_qkv[2 * D:3 * D]).reshape(V, H, Dh)
-    k = rope_neox(qk_rms_norm(k, blk["k_g"], dims.qk_eps), pos[:V], dims.rope_base)
+    k = st("qkv", linear(h[kv_rows], w_qkv[D:2 * D])).reshape(V, H, Dh)
+    v = st("qkv", linear(h[kv_rows], w_qkv[2 * D:3 * D])).reshape(V, H, Dh)
+    k = st("qk", rope_neox(qk_rms_norm(k, blk["k_g"], dims.qk_eps), pos[:V], dims.rope_base))
 
     if rows is None:
         rows = np.arange(L)
     rows = np.asarray(rows, dtype=np.int64)
     sel_valid = rows[rows < V]
 
-    q = linear(h[sel_valid], w_qkv[0:D]).reshape(len(sel_valid), H, Dh)
-    q = rope_neox(qk_rms_norm(q, blk["q_g"], dims.qk_eps), pos[sel_valid], dims.rope_base)
-    o = attention_rows(q, k, v, V).reshape(len(sel_valid), D) if V > 0 else np.zeros((0, D))
+    q = st("qkv", linear(h[sel_valid], w_qkv[0:D])).reshape(len(sel_valid), H, Dh)
+    q = st("qk", rope_neox(qk_rms_norm(q, blk["q_g"], dims.qk_eps), pos[sel_valid], dims.rope_base))
+    p_store = None if store is None else (lambda p: st("p", p))
+    o = (attention_rows(q, k, v, V, p_store).reshape(len(sel_valid), D) if V > 0
+         else np.zeros((0, D)))
+    o = st("o", o)
 
     ms = mod[sel_valid]
     Es = E[ms]                                              # [R, 6, D]
     y = linear(o, blk["w_o"])
-    x1 = x[sel_valid] + Es[:, GATE_MSA] * y
+    x1 = st("x1", x[sel_valid] + Es[:, GATE_MSA] * y)
     x1n = rms_normalize(x1, dims.norm_eps) * np.asarray(blk["norm2_g"], dtype=F64)
-    h2 = x1n * (1.0 + Es[:, SCALE_MLP]) + Es[:, SHIFT_MLP]
-    a = swiglu(h2, blk["w_gate_up"], F)
+    h2 = st("h2", x1n * (1.0 + Es[:, SCALE_MLP]) + Es[:, SHIFT_MLP])
+    a = st("act", swiglu(h2, blk["w_gate_up"], F))
     z = linear(a, blk["w_down"])
-    x2_sel = x1 + Es[:, GATE_MLP] * z
+    x2_sel = st("out", x1 + Es[:, GATE_MLP] * z)
 
     out = np.zeros((len(rows), D), dtype=F64)
     idx = np.nonzero(rows < V)[0]
@@ -307,6 +334,43 @@ def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
     inter = dict(h=h[sel_valid], q=q.reshape(len(sel_valid), D), o=o, x1=x1, h2=h2, a=a,
                  k=k.reshape(V, D), v=v.reshape(V, D), rows_valid=sel_valid)
     return out, inter
+
+
+# Intermediates a bf16 implementation stores as bf16: the operands of every bf16 matrix
+# product (h, the q/k/v projections, q and k after norm + RoPE, the attention probabilities, the
+# attention output, h2 and the SwiGLU output). The mid-block residual x1 is kept in fp32.
+BF16_STORED = ("h", "qkv", "qk", "p", "o", "h2", "act")
+
+
+def block_forward_bf16_storage(x, blk: dict, temb, dims: Dims, layout: Layout,
+                               positions: Optional[np.ndarray] = None,
+                               rows: Optional[np.ndarray] = None,
+                               out_bf16: bool = True) -> np.ndarray:
+    """DIAGNOSTIC, never the graded reference: ``block_forward`` with every intermediate in
+    ``BF16_STORED`` (and, when out_bf16, the block output) rounded to bf16 where it is stored,
+    all arithmetic between the roundings exact (float64).
+
+    [P3 "Changes Made"]: the H3 DiT runs in BF16 with explicit BF16/FP32 boundaries; the
+    matrix products take bf16 operands. The difference between this function and
+    ``block_forward`` is the error that bf16 storage alone causes, with no arithmetic error
+    of any kernel; it is what a tolerance on a bf16 implementation is derived from.
+    """
+    names = BF16_STORED + (("out",) if out_bf16 else ())
+
+    def store(name, a):
+        return bf16_round(a) if name in names else a
+
+    return block_forward(x, blk, temb, dims, layout, positions, rows, store=store)
+
+
+def attention_bf16_storage(q, k, v, n_valid: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """DIAGNOSTIC, never the graded reference: ``attention_valid`` (or ``attention_rows`` for
+    the query rows ``rows``) with the probabilities stored as bf16 before they weight the
+    values and are summed, and the output rounded to bf16."""
+    if rows is None:
+        return bf16_round(attention_valid(q, k, v, n_valid, p_store=bf16_round))
+    q = np.asarray(q, dtype=F64)
+    return bf16_round(attention_rows(q[rows], k, v, n_valid, p_store=bf16_round))
 
 
 def stack_forward(x, blocks: Sequence[dict], temb, dims: Dims, layout: Layout,

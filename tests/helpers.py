@@ -32,42 +32,94 @@ def close_stats(got, ref):
 
 
 def bf16_floor(ref) -> float:
-    """max |bf16(ref) - ref|: the error of the exact result correctly rounded to bf16, the
-    smallest max error any bf16 output can have."""
+    """max |bf16(ref) - ref|: the error of the exact result correctly rounded to bf16 (reported
+    only)."""
     ref = np.asarray(ref, dtype=np.float64)
     return float(np.max(np.abs(O.bf16_round(ref) - ref))) if ref.size else 0.0
 
 
-# A bf16 block output carries its own rounding (up to one "floor", the error of the exact value
-# correctly rounded to bf16, reached at the largest elements) plus the bf16 roundings of the five
-# intermediates the block stores (h, q/k/v, o, h2, act), which reach the largest outputs through
-# the gated residuals: measured 1.5 floors in total at the 13,440-token block and 2.1 at the
-# 4,608-token loop block. Three floors bound that with a margin.
-BF16_FLOORS = 3.0
-# An fp32 block output (the fp32 residual stream) has no rounding of its own but carries the
-# same bf16 intermediates: two floors of the reference (measured 1.15 at the 13,440-token block).
-FP32_BLOCK_FLOORS = 2.0
+def bf16_ulp(a: float) -> float:
+    """Spacing of the bf16 values at magnitude a (8 significant bits): 2^(floor(log2 a) - 7)."""
+    if not a > 0:
+        return 0.0
+    return math.ldexp(1.0, math.frexp(a)[1] - 8)
 
 
-def assert_close(got, ref, name: str, rel=REL_MAX_ERR, min_cos=MIN_COSINE, bf16_out=True,
-                 bf16_intermediates=False):
-    """Floating-point parity bar for block outputs and loop latents: max |err| <= 2e-2 * RMS(ref)
-    and cosine >= 0.9995. For a bf16 output whose exact value, correctly rounded to bf16,
-    already exceeds 2e-2 * RMS (heavy-tailed outputs: half an ulp at max |ref| is larger than
-    2e-2 * RMS once max |ref| > ~5 RMS), the max-error bound is BF16_FLOORS times that rounding
-    floor; for an fp32 block output computed through bf16 intermediates (bf16_out=False,
-    bf16_intermediates=True) it is FP32_BLOCK_FLOORS times the floor."""
+def assert_close(got, ref, name: str, rel=REL_MAX_ERR, min_cos=MIN_COSINE):
+    """The stated floating-point bar, with no allowance: max |err| <= 2e-2 * RMS(ref) and
+    cosine >= 0.9995 (loop latents, velocities, any output not judged through the storage
+    diagnostic)."""
     err, rms, cos = close_stats(got, ref)
-    floors = BF16_FLOORS if bf16_out else (FP32_BLOCK_FLOORS if bf16_intermediates else 0.0)
-    floor = bf16_floor(ref) if floors else 0.0
-    bound = max(rel * rms, floors * floor)
-    which = "2e-2*RMS" if bound == rel * rms else f"{floors:g}*bf16 floor"
     say(f"  {name}: max|err| {err:.3e}  RMS(ref) {rms:.3e}  ratio {err / max(rms, 1e-30):.2e}  "
-        f"bf16 floor {floor / max(rms, 1e-30):.2e}*RMS  bound {which}  cos {cos:.7f}")
+        f"bound 2e-2*RMS  cos {cos:.7f}")
     assert np.all(np.isfinite(np.asarray(got))), f"{name}: non-finite values"
-    assert err <= bound, f"{name}: max|err| {err:.3e} > bound {bound:.3e} ({which})"
+    assert err <= rel * rms, f"{name}: max|err| {err:.3e} > 2e-2*RMS {rel * rms:.3e}"
     assert cos >= min_cos, f"{name}: cosine {cos:.7f} < {min_cos}"
     return err / max(rms, 1e-30), cos
+
+
+def assert_storage_close(got, exact, diag, name: str, rel=REL_MAX_ERR, min_cos=MIN_COSINE):
+    """Parity of an output computed through bf16-stored intermediates, judged with the oracle's
+    bf16-storage diagnostic ``diag`` (the same function with each stored intermediate rounded to
+    bf16 and exact arithmetic in between) beside the exact oracle ``exact``. Rules, fixed before
+    any GPU run:
+
+      (a) max |got - diag| <= U, U = one bf16 ulp at max |diag|: the kernels differ from the
+          storage model only by fp32 arithmetic, which moves a stored value across a rounding
+          midpoint now and then (one ulp of that value) and changes the rest far below an ulp.
+      (b) max |got - exact| <= max(2e-2 RMS(exact), E_s + U), E_s = max |diag - exact| (the
+          error bf16 storage alone causes, computed by the oracle), and cosine >= 0.9995. When
+          (a) holds, (b) follows by the triangle inequality; it is the graded bar, widened only
+          by what the storage diagnostic accounts for."""
+    got = np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    diag = np.asarray(diag, dtype=np.float64)
+    err, rms, cos = close_stats(got, exact)
+    e_s = float(np.max(np.abs(diag - exact))) if exact.size else 0.0
+    d_gd = float(np.max(np.abs(got - diag))) if exact.size else 0.0
+    u = bf16_ulp(float(np.max(np.abs(diag)))) if exact.size else 0.0
+    bound = max(rel * rms, e_s + u)
+    which = "2e-2*RMS" if bound == rel * rms else "E_s+U"
+    r = max(rms, 1e-30)
+    same = float(np.mean(got == diag)) if exact.size else 1.0
+    say(f"  {name}: max|err| {err / r:.2e}*RMS (RMS {rms:.3e})  storage E_s {e_s / r:.2e}*RMS  "
+        f"U {u / r:.2e}*RMS  max|got-diag| {d_gd / max(u, 1e-30):.2f} U  equal to diag {same:.4f}  "
+        f"bound {which} {bound / r:.2e}*RMS  bf16 floor {bf16_floor(exact) / r:.2e}*RMS  "
+        f"cos {cos:.7f}")
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert d_gd <= u, f"{name}: max|got - diag| {d_gd:.3e} > one bf16 ulp {u:.3e}"
+    assert err <= bound, f"{name}: max|err| {err:.3e} > bound {bound:.3e} ({which})"
+    assert cos >= min_cos, f"{name}: cosine {cos:.7f} < {min_cos}"
+    return err / r, cos
+
+
+def check_block(got, x, bp, temb, wl, name: str, rows=None, positions=None, out_bf16=True,
+                layout=None):
+    """A block output (all rows of the layout, or the rows ``rows``) against the exact oracle
+    and the bf16-storage diagnostic, valid rows only; returns the exact reference rows."""
+    blk = oracle_block(bp)
+    dims = oracle_dims(wl)
+    lay = oracle_layout(wl) if layout is None else layout
+    x = np.asarray(x, dtype=np.float64)
+    exact = O.block_forward(x, blk, temb, dims, lay, positions=positions, rows=rows)
+    diag = O.block_forward_bf16_storage(x, blk, temb, dims, lay, positions=positions, rows=rows,
+                                        out_bf16=out_bf16)
+    sel = np.arange(lay.seq_pad) if rows is None else np.asarray(rows)
+    keep = sel < lay.n_valid
+    assert_storage_close(np.asarray(got)[keep], exact[keep], diag[keep], name)
+    return exact
+
+
+def check_attention(got, q, k, v, n_valid: int, name: str, rows=None):
+    """An attention output (bf16, rows < n_valid, or the query rows ``rows``) against the exact
+    oracle and the storage diagnostic (probabilities and output stored as bf16)."""
+    if rows is None:
+        exact = O.attention_valid(q, k, v, n_valid)[:n_valid]
+        diag = O.attention_bf16_storage(q, k, v, n_valid)[:n_valid]
+    else:
+        exact = O.attention_rows(np.asarray(q, dtype=np.float64)[rows], k, v, n_valid)
+        diag = O.attention_bf16_storage(q, k, v, n_valid, rows=rows)
+    assert_storage_close(got, exact, diag, name)
 
 
 # Per-kernel bar for an intermediate stored in bf16 and fed the GPU's own input: a bf16 store

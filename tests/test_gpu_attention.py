@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from helpers import assert_close, say
+from helpers import assert_close, check_attention, say
 
 pytestmark = pytest.mark.gpu
 
@@ -48,14 +48,14 @@ def test_attention_ragged_small(N, head_dim):
     L, H = 300, 2
     say(f"attention ragged small: L={L} H={H} Dh={head_dim} valid={valid}")
     q, k, v = attention_case(len(valid), L, H, head_dim, valid, seed=1)
-    ref = _oracle(q, k, v, valid)
     got_vo = _run(N, q, k, v, valid, N.DIT_ATTN_VALID_ONLY, o_fill=0x7FC0)
     got_fv = _run(N, q, k, v, valid, N.DIT_ATTN_FIXED_VALID, o_fill=0x7FC0)
     assert np.array_equal(got_vo, got_fv), "fixed-valid and valid-only must agree bit for bit"
     for b, n in enumerate(valid):
         assert np.all(got_vo[b, n:] == 0), f"request {b}: tail rows must be exactly 0"
         if n:
-            assert_close(bf16_to_f32(got_vo[b, :n]), ref[b, :n], f"req {b} (valid {n})")
+            check_attention(bf16_to_f32(got_vo[b, :n]), bf16_to_f32(q[b]), bf16_to_f32(k[b]),
+                            bf16_to_f32(v[b]), n, f"req {b} (valid {n})")
 
 
 def test_attention_tail_garbage_is_ignored(N):
@@ -119,8 +119,8 @@ def test_attention_ragged_batch_full_size(N):
     for b, n in enumerate(valid):
         assert np.all(vo[b, n:] == 0)
         rows = np.sort(np.concatenate([rng.choice(n, 22, replace=False), [0, n - 1]]))
-        ref = O.attention_rows(bf16_to_f32(q[b, rows]), bf16_to_f32(k[b]), bf16_to_f32(v[b]), n)
-        assert_close(bf16_to_f32(vo[b, rows]), ref, f"request {b} (valid {n}), sampled rows")
+        check_attention(bf16_to_f32(vo[b, rows]), bf16_to_f32(q[b]), bf16_to_f32(k[b]),
+                        bf16_to_f32(v[b]), n, f"request {b} (valid {n}), sampled rows", rows=rows)
 
 
 @pytest.mark.parametrize("head_dim,gain", [(64, 1.0), (128, 1.0), (128, 1.9), (128, 6.0)])
@@ -147,7 +147,6 @@ def test_attention_with_qk_norm_gains(N, head_dim, gain):
         return bf16_bits(y.astype(np.float32))
 
     qn, kn = qk_norm(q, gq), qk_norm(k, gk)
-    ref = _oracle(qn, kn, v, valid)
     got = _run(N, qn, kn, v, valid, N.DIT_ATTN_VALID_ONLY, o_fill=0x7FC0, gains=(gq, gk))
     got_fv = _run(N, qn, kn, v, valid, N.DIT_ATTN_FIXED_VALID, o_fill=0x7FC0, gains=(gq, gk))
     assert np.array_equal(got, got_fv), "fixed-valid and valid-only must agree bit for bit"
@@ -158,4 +157,5 @@ def test_attention_with_qk_norm_gains(N, head_dim, gain):
     assert np.array_equal(got, got_g), "tail contents must not change the outputs"
     for b, n in enumerate(valid):
         assert np.all(got[b, n:] == 0)
-        assert_close(bf16_to_f32(got[b, :n]), ref[b, :n], f"req {b} (valid {n}, gain {gain})")
+        check_attention(bf16_to_f32(got[b, :n]), bf16_to_f32(qn[b]), bf16_to_f32(kn[b]),
+                        bf16_to_f32(v[b]), n, f"req {b} (valid {n}, gain {gain})")

@@ -4,7 +4,7 @@ requests' own dit_block_forward calls bit for bit, and matches the oracle."""
 import numpy as np
 import pytest
 
-from helpers import assert_close, oracle_block, oracle_dims, say
+from helpers import check_block, say
 
 pytestmark = pytest.mark.gpu
 
@@ -72,8 +72,8 @@ def test_batched_small_ragged_equals_single_requests(env):
     lay = O.Layout(nv, na, L)
     xs = bf16_to_f32(x[b * L:(b + 1) * L]).astype(np.float64)
     xs[nv + na:] = 0
-    ref = O.block_forward(xs, oracle_block(blk_p), temb[b], oracle_dims(wl), lay, positions=pos)
-    assert_close(bf16_to_f32(got[b * L: b * L + nv + na]), ref[:nv + na], "request 2 vs oracle")
+    check_block(bf16_to_f32(got[b * L:(b + 1) * L]), xs, blk_p, temb[b], wl, "request 2 vs oracle",
+                positions=pos, layout=lay)
 
 
 def test_batched_h3_scale_equals_single_requests(env):
@@ -110,9 +110,8 @@ def test_batched_block_ragged_full_size(env):
         rows = np.sort(np.concatenate([rng.choice(V, 20, replace=False), [0, nv - 1, nv, V - 1]]))
         xs = I.bf16_to_f32(x[b * L:(b + 1) * L]).astype(np.float64)
         xs[V:] = 0
-        ref = O.block_forward(xs, oracle_block(blk_p), temb[b], oracle_dims(wl), O.Layout(nv, na, L),
-                              rows=rows)
-        assert_close(I.bf16_to_f32(got[b * L + rows]), ref, f"request {b} sampled rows vs oracle")
+        check_block(I.bf16_to_f32(got[b * L + rows]), xs, blk_p, temb[b], wl,
+                    f"request {b} sampled rows vs oracle", rows=rows, layout=O.Layout(nv, na, L))
 
 
 def test_batched_fixed_valid_equals_valid_only(env):

@@ -5,7 +5,7 @@ import dataclasses
 import numpy as np
 import pytest
 
-from helpers import (assert_close, assert_kernel_close, oracle_block, oracle_dims, oracle_layout,
+from helpers import (assert_kernel_close, check_block, oracle_block, oracle_dims, oracle_layout,
                      say, x_values)
 
 pytestmark = pytest.mark.gpu
@@ -74,9 +74,8 @@ def test_block_end_to_end_and_per_kernel(env, name):
     blk = oracle_block(case.blocks[0])
     dims, lay = oracle_dims(wl), oracle_layout(wl)
     x = x_values(case.x)
-    ref = O.block_forward(x, blk, case.temb, dims, lay)
     assert np.all(got[V:] == 0), "tail rows of the block output must be exactly 0"
-    assert_close(got[:V], ref[:V], f"{name} block output (end to end)")
+    check_block(got, x, case.blocks[0], case.temb, wl, f"{name} block output (end to end)")
 
     # teacher-forced per-kernel checks: each kernel against the oracle step fed with the GPU's
     # own input to that step
@@ -165,9 +164,8 @@ def test_block_h3_sampled_rows(env):
     assert np.all(got[V:] == 0)
     rng = np.random.default_rng(11)
     rows = np.sort(np.concatenate([rng.choice(V, 44, replace=False), [0, wl.n_video - 1, wl.n_video, V - 1]]))
-    ref = O.block_forward(x_values(case.x), oracle_block(case.blocks[0]), case.temb,
-                          oracle_dims(wl), oracle_layout(wl), rows=rows)
-    assert_close(got[rows], ref, "block_h3 sampled rows")
+    check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl, "block_h3 sampled rows",
+                rows=rows)
 
 
 @pytest.mark.parametrize("name,gain,path", [("block_small", 1.2, "shift-free"),
@@ -200,9 +198,8 @@ def test_block_attention_softmax_paths(env, name, gain, path):
     got = dev.bf16_values_of(out).astype(np.float64)
     blk = oracle_block(blk_p)
     dims, lay = oracle_dims(wl), oracle_layout(wl)
-    ref = O.block_forward(x_values(case.x), blk, case.temb, dims, lay)
     assert np.all(got[V:] == 0)
-    assert_close(got[:V], ref[:V], f"{name} block output ({path} softmax path)")
+    check_block(got, x_values(case.x), blk_p, case.temb, wl, f"{name} block output ({path} softmax path)")
     it = _inter(dev, ws, m, wl)
     q_g = it["qkv"][:V, :D].reshape(V, H, Dh)
     k_g = it["qkv"][:V, D:2 * D].reshape(V, H, Dh)

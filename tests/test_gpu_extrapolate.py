@@ -58,7 +58,7 @@ def test_loop_extrapolate_matches_oracle(env, residual_f32):
                             ref_hits, input_bf16=not residual_f32, extrapolate=True)
     V = wl.n_valid
     assert np.all(got[V:] == 0)
-    assert_close(got[:V], ref[:V], "final latent (extrapolated reuse)", bf16_out=False)
+    assert_close(got[:V], ref[:V], "final latent (extrapolated reuse)")
     plain, _, _ = _loop(env, case, N.make_policy("velocity", 0.0, 1.0, 3, 2), residual_f32)
     assert not np.array_equal(plain, got)
 

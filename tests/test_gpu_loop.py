@@ -3,7 +3,7 @@
 import numpy as np
 import pytest
 
-from helpers import assert_close, close_stats, oracle_block, oracle_dims, oracle_layout, say
+from helpers import assert_close, check_block, oracle_block, oracle_dims, oracle_layout, say
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +89,7 @@ def test_loop_small_free_running(env, mode):
                             O.row_modality(lay), ref_hits)
     V = wl.n_valid
     assert np.all(got[V:] == 0)
-    assert_close(got[:V], ref[:V], f"final latent ({mode})", bf16_out=False)
+    assert_close(got[:V], ref[:V], f"final latent ({mode})")
 
 
 def _composed(env, case, hits, check_steps=(), rows=None):
@@ -97,7 +97,6 @@ def _composed(env, case, hits, check_steps=(), rows=None):
     in check_steps every block is compared (sampled rows) with the oracle block fed the GPU's
     own block input."""
     import torch
-    import oracle as O
     from audio_video_diffusion_dit_amd import inputs as I
     N, dev = env
     wl = case.wl
@@ -120,11 +119,9 @@ def _composed(env, case, hits, check_steps=(), rows=None):
                 N.dit_block_forward(dims, lay, blocks[b].weights, temb[i], cur, out, 0, ws)
                 if i in check_steps:
                     torch.cuda.synchronize()
-                    ref = O.block_forward(dev.bf16_values_of(cur).astype(np.float64),
-                                          oracle_block(case.blocks[b]), case.temb_steps[i],
-                                          oracle_dims(wl), oracle_layout(wl), rows=rows)
-                    assert_close(dev.bf16_values_of(out)[rows], ref,
-                                 f"interval {i} block {b} (sampled rows, teacher-forced)")
+                    check_block(dev.bf16_values_of(out)[rows], dev.bf16_values_of(cur),
+                                case.blocks[b], case.temb_steps[i], wl,
+                                f"interval {i} block {b} (sampled rows, teacher-forced)", rows=rows)
                 cur = out
         N.step_update(x, v, xb, lay, D, float(np.float32(sv[i + 1]) - np.float32(sv[i])),
                       float(np.float32(sa[i + 1]) - np.float32(sa[i])))

@@ -6,7 +6,7 @@ import dataclasses
 import numpy as np
 import pytest
 
-from helpers import assert_close, assert_kernel_close, oracle_block, oracle_dims, oracle_layout, say
+from helpers import assert_close, assert_kernel_close, check_block, oracle_block, oracle_dims, oracle_layout, say
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +71,8 @@ def test_block_f32_end_to_end(env, name):
     xv = np.where(np.arange(wl.seq_pad)[:, None] < V, x, 0).astype(np.float64)
     ref = O.block_forward(xv, blk, case.temb, dims, lay)
     assert np.all(got[V:] == 0) and np.all(x1[V:] == 0)
-    assert_close(got[:V], ref[:V], f"{name} fp32-residual block output", bf16_out=False,
-                 bf16_intermediates=True)
+    check_block(got, xv, case.blocks[0], case.temb, wl, f"{name} fp32-residual block output",
+                out_bf16=False)
     # x1 = x + gate_msa * (o Wo^T) from the oracle's own attention output: compare loosely (the
     # GPU's o carries bf16 roundings), as a per-kernel intermediate
     mod = O.row_modality(lay)
@@ -121,11 +121,9 @@ def test_block_f32_h3_sampled_rows(env):
     rows = np.sort(np.concatenate([np.random.default_rng(4).choice(V, 40, replace=False),
                                    [0, wl.n_video - 1, wl.n_video, V - 1]]))
     xv = np.where(np.arange(wl.seq_pad)[:, None] < V, x, 0).astype(np.float64)
-    ref = O.block_forward(xv, oracle_block(case.blocks[0]), case.temb, oracle_dims(wl),
-                          oracle_layout(wl), rows=rows)
     assert np.all(got[V:] == 0)
-    assert_close(got[rows], ref, "block_h3 fp32-residual output (sampled rows)", bf16_out=False,
-                 bf16_intermediates=True)
+    check_block(got[rows], xv, case.blocks[0], case.temb, wl,
+                "block_h3 fp32-residual output (sampled rows)", rows=rows, out_bf16=False)
 
 
 def _loop(env, case, mode, residual_f32):
@@ -166,7 +164,7 @@ def test_loop_nonlinear_per_modality_schedules(env, residual_f32):
                             O.row_modality(lay), ref_hits, input_bf16=not residual_f32)
     V = wl.n_valid
     assert np.all(got[V:] == 0)
-    assert_close(got[:V], ref[:V], "final latent", bf16_out=False)
+    assert_close(got[:V], ref[:V], "final latent")
 
 
 def test_loop_f32_is_closer_to_the_unrounded_oracle(env):

@@ -9,6 +9,7 @@ the CPU only.
 import json
 import math
 import os
+import struct
 
 import numpy as np
 import pytest
@@ -292,9 +293,31 @@ def test_swiglu_gate_rows_first():
 
 # -------------------------------------------------------- block (brute) -----
 
-def _block_brute(x, blk, temb, D, H, Dh, F, n_video, n_audio, L, eps, qk_eps, base, count):
-    """Scalar-loop block written directly from the block's definition."""
+def _bf16_scalar(v):
+    """A float64 value converted to fp32 (round to nearest even, as C converts), then to the
+    nearest bfloat16 with ties to even, found by bracketing: bf16 keeps 8 significant bits."""
+    f = struct.unpack("<f", struct.pack("<f", v))[0]
+    if f == 0.0 or not math.isfinite(f):
+        return f
+    m, e = math.frexp(f)              # f = m 2^e, 0.5 <= |m| < 1
+    scaled = abs(m) * 256.0           # in [128, 256): exactly representable in float64
+    lo = math.floor(scaled)
+    frac = scaled - lo
+    if frac > 0.5 or (frac == 0.5 and lo % 2 == 1):
+        lo += 1
+    return math.copysign(lo * 2.0 ** (e - 8), f)
+
+
+def _block_brute(x, blk, temb, D, H, Dh, F, n_video, n_audio, L, eps, qk_eps, base, count,
+                 rnd=None):
+    """Scalar-loop block written directly from the block's definition. With rnd, every
+    stored intermediate (h, the q/k/v projections, q and k after RoPE, the attention weights
+    before they are summed, the attention output, h2, the SwiGLU output and the output) is
+    passed through rnd element by element."""
     V = n_video + n_audio
+    if rnd is None:
+        rnd = lambda t: t
+    R = lambda vec: [rnd(t) for t in vec]
 
     def mod_of(r):
         return 0 if r < n_video else 1
@@ -321,8 +344,8 @@ def _block_brute(x, blk, temb, D, H, Dh, F, n_video, n_audio, L, eps, qk_eps, ba
     for r in range(V):
         m = mod_of(r)
         n = rmsn([float(t) for t in x[r]], blk["norm1_g"])
-        h = [n[d] * (1.0 + E(m, 1, d)) + E(m, 0, d) for d in range(D)]
-        qkv = matvec(blk["w_qkv"], h, 3 * D)
+        h = R([n[d] * (1.0 + E(m, 1, d)) + E(m, 0, d) for d in range(D)])
+        qkv = R(matvec(blk["w_qkv"], h, 3 * D))
         per = []
         for part in range(2):
             vec = qkv[part * D:(part + 1) * D]
@@ -338,7 +361,7 @@ def _block_brute(x, blk, temb, D, H, Dh, F, n_video, n_audio, L, eps, qk_eps, ba
                     c, s = math.cos(ang), math.sin(ang)
                     rot[i] = hv[i] * c - hv[i + Dh // 2] * s
                     rot[i + Dh // 2] = hv[i + Dh // 2] * c + hv[i] * s
-                heads.append(rot)
+                heads.append(R(rot))
             per.append(heads)
         qs.append(per[0])
         ks.append(per[1])
@@ -354,20 +377,20 @@ def _block_brute(x, blk, temb, D, H, Dh, F, n_video, n_audio, L, eps, qk_eps, ba
                 sc.append(sum(qs[r][hh][d] * ks[j][hh][d] for d in range(Dh)) / math.sqrt(Dh))
                 count[0] += 2 * Dh
             mx = max(sc)
-            w = [math.exp(t - mx) for t in sc]
+            w = R([math.exp(t - mx) for t in sc])
             tot = sum(w)
             for d in range(Dh):
-                o.append(sum(w[j] * vs[j][hh][d] for j in range(V)) / tot)
+                o.append(rnd(sum(w[j] * vs[j][hh][d] for j in range(V)) / tot))
                 count[0] += 2 * V
         y = matvec(blk["w_o"], o, D)
         x1 = [float(x[r, d]) + E(m, 2, d) * y[d] for d in range(D)]
         n2 = rmsn(x1, blk["norm2_g"])
-        h2 = [n2[d] * (1.0 + E(m, 4, d)) + E(m, 3, d) for d in range(D)]
+        h2 = R([n2[d] * (1.0 + E(m, 4, d)) + E(m, 3, d) for d in range(D)])
         gu = matvec(blk["w_gate_up"], h2, 2 * F)
-        a = [gu[i] / (1.0 + math.exp(-gu[i])) * gu[F + i] for i in range(F)]
+        a = R([gu[i] / (1.0 + math.exp(-gu[i])) * gu[F + i] for i in range(F)])
         z = matvec(blk["w_down"], a, D)
         for d in range(D):
-            out[r, d] = x1[d] + E(m, 5, d) * z[d]
+            out[r, d] = rnd(x1[d] + E(m, 5, d) * z[d])
     return out
 
 
@@ -405,6 +428,65 @@ def test_block_against_scalar_loops():
     # subset rows agree with the full result
     sub = O.block_forward(x, blk, temb, dims, lay, rows=np.array([0, 4, 6]))
     assert np.allclose(sub, got[[0, 4, 6]], rtol=1e-13, atol=1e-14)
+
+
+def test_bf16_scalar_rounding_reference():
+    # the bracketing rounding used by the scalar loops agrees with hand-derived cases
+    assert _bf16_scalar(1.0) == 1.0
+    assert _bf16_scalar(1.0 + 2 ** -8) == 1.0                   # tie, 1.0 is even
+    assert _bf16_scalar(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6     # tie, rounds to the even 2^-6 step
+    assert _bf16_scalar(1.0 + 2 ** -8 + 2 ** -20) == 1.0 + 2 ** -7
+    assert _bf16_scalar(-3.0 - 2 ** -7) == -3.0                 # tie; -3 = -192 * 2^-6 is even
+    assert _bf16_scalar(255.5) == 256.0
+
+
+def test_block_bf16_storage_diagnostic_against_scalar_loops():
+    """The storage diagnostic equals the scalar-loop block with each stored intermediate rounded
+    to bf16 element by element; without the output rounding only the output differs; and its
+    distance from the exact block is of the size bf16 storage causes (well above float64
+    rounding, well below the values)."""
+    D, H, Dh, F = 8, 2, 4, 6
+    n_v, n_a, L = 3, 2, 7
+    blk, temb = _tiny_block(17, D, H, Dh, F)
+    rng = np.random.default_rng(18)
+    x = np.zeros((L, D))
+    x[: n_v + n_a] = rng.standard_normal((n_v + n_a, D))
+    dims = O.Dims(D, H, Dh, F, rope_base=100.0)
+    lay = O.Layout(n_v, n_a, L)
+    got = O.block_forward_bf16_storage(x, blk, temb, dims, lay)
+    want = _block_brute(x, blk, temb, D, H, Dh, F, n_v, n_a, L, 1e-6, 1e-6, 100.0, [0],
+                        rnd=_bf16_scalar)
+    assert np.array_equal(got, want)
+    # every stored output value is a bf16 value
+    assert np.array_equal(O.bf16_round(got), got)
+    # fp32 output: no final rounding
+    got32 = O.block_forward_bf16_storage(x, blk, temb, dims, lay, out_bf16=False)
+    assert np.array_equal(O.bf16_round(got32), got)
+    exact = O.block_forward(x, blk, temb, dims, lay)
+    rel = np.max(np.abs(got32 - exact)) / np.sqrt(np.mean(exact[: n_v + n_a] ** 2))
+    assert 1e-5 < rel < 3e-2, rel
+    # the row-subset form agrees with the full form
+    sub = O.block_forward_bf16_storage(x, blk, temb, dims, lay, rows=np.array([1, 3, 6]))
+    assert np.array_equal(sub, got[[1, 3, 6]])
+
+
+def test_attention_bf16_storage_diagnostic():
+    """Attention with the probabilities stored as bf16 equals the scalar-loop softmax with the
+    weights rounded before the sum, output rounded; rows form = full form."""
+    rng = np.random.default_rng(19)
+    L, n, H, Dh = 9, 7, 2, 4
+    q, k, v = (rng.standard_normal((L, H, Dh)) for _ in range(3))
+    got = O.attention_bf16_storage(q, k, v, n)
+    for h in range(H):
+        for i in range(n):
+            sc = [sum(q[i, h, d] * k[j, h, d] for d in range(Dh)) / math.sqrt(Dh) for j in range(n)]
+            mx = max(sc)
+            w = [_bf16_scalar(math.exp(t - mx)) for t in sc]
+            for d in range(Dh):
+                o = sum(w[j] * v[j, h, d] for j in range(n)) / sum(w)
+                assert got[i, h, d] == _bf16_scalar(o)
+    assert np.all(got[n:] == 0)
+    assert np.array_equal(O.attention_bf16_storage(q, k, v, n, rows=np.array([0, 5])), got[[0, 5]])
 
 
 def test_block_zero_gates_is_identity():
