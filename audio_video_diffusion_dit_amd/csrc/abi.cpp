@@ -139,11 +139,57 @@ void build_map(const dit_dims* d, const dit_layout* l, int32_t n_blocks, dit_wor
   m->total = off < kAlign ? kAlign : off;
 }
 
+int check_weight_alignment(const dit_block_weights* w, int idx);
+
 int check_weights(const dit_block_weights* w, int idx) {
   if (!w) return fail(DIT_ERR_INVALID, "block %d weights are null", idx);
   if (!w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->norm1_g || !w->norm2_g ||
       !w->q_g || !w->k_g || !w->ada)
     return fail(DIT_ERR_INVALID, "block %d has a null weight pointer", idx);
+  return check_weight_alignment(w, idx);
+}
+
+// The kernels address their large operands through buffer resources with 32-bit byte offsets,
+// so each operand must span less than 2 GiB. Checked before anything is enqueued.
+constexpr int64_t kMaxSpan = (int64_t)1 << 31;
+
+int check_span(int64_t bytes, const char* what) {
+  if (bytes >= kMaxSpan)
+    return fail(DIT_ERR_UNSUPPORTED,
+                "%s spans %lld bytes; the kernels address at most 2 GiB - 1 per operand", what,
+                (long long)bytes);
+  return DIT_OK;
+}
+
+// Operand spans of one block over rows_total rows (a batch: all requests), seq_pad rows per
+// request: the projection weights, the activations the GEMMs read, and one request's q/k/v rows
+// that attention reads.
+int check_block_spans(const dit_dims* d, int64_t rows_total, int64_t seq_pad) {
+  const int64_t D = d->hidden, F = d->ffn;
+  int st;
+  if ((st = check_span(3 * D * D * 2, "the qkv weight [3D, D]")) != DIT_OK) return st;
+  if ((st = check_span(2 * F * D * 2, "the gate/up weight [2F, D]")) != DIT_OK) return st;
+  if ((st = check_span(D * F * 2, "the down weight [D, F]")) != DIT_OK) return st;
+  if ((st = check_span(rows_total * D * 2, "the block activations [rows, D]")) != DIT_OK) return st;
+  if ((st = check_span(rows_total * ffn_ld(d) * 2, "the SwiGLU activations [rows, F]")) != DIT_OK)
+    return st;
+  if ((st = check_span(seq_pad * 3 * D * 2, "one request's q/k/v rows [seq_pad, 3D]")) != DIT_OK)
+    return st;
+  return DIT_OK;
+}
+
+// Pointers the kernels read or write with 16-byte vector accesses.
+int check_aligned16(const void* p, const char* what) {
+  if (((uintptr_t)p & 15) != 0) return fail(DIT_ERR_INVALID, "%s must be 16-byte aligned", what);
+  return DIT_OK;
+}
+
+int check_weight_alignment(const dit_block_weights* w, int idx) {
+  const void* ptrs[] = {w->norm1_g, w->norm2_g, w->q_g, w->k_g, w->ada};
+  const char* names[] = {"norm1_g", "norm2_g", "q_g", "k_g", "ada"};
+  for (int i = 0; i < 5; ++i)
+    if (((uintptr_t)ptrs[i] & 15) != 0)
+      return fail(DIT_ERR_INVALID, "block %d: %s must be 16-byte aligned", idx, names[i]);
   return DIT_OK;
 }
 
@@ -284,6 +330,7 @@ size_t dit_workspace_size(const dit_dims* dims, const dit_layout* layout, int32_
     fail(DIT_ERR_INVALID, "n_blocks must be >= 0");
     return 0;
   }
+  if (check_block_spans(dims, layout->seq_pad, layout->seq_pad) != DIT_OK) return 0;
   dit_workspace_map m;
   build_map(dims, layout, n_blocks, &m);
   if (map) *map = m;
@@ -306,8 +353,10 @@ int block_forward_impl(const dit_dims* dims, const dit_layout* layout,
   if (!temb || !x_in || !x_out) return fail(DIT_ERR_INVALID, "temb, x_in and x_out must be non-null");
   if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
     return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
-  if (f32 && ((((uintptr_t)x_in) & 15) || (((uintptr_t)x_out) & 15)))
-    return fail(DIT_ERR_INVALID, "x_in and x_out must be 16-byte aligned");
+  if ((st = check_aligned16(x_in, "x_in")) != DIT_OK) return st;
+  if ((st = check_aligned16(x_out, "x_out")) != DIT_OK) return st;
+  if ((st = check_aligned16(temb, "temb")) != DIT_OK) return st;
+  if ((st = check_block_spans(dims, layout->seq_pad, layout->seq_pad)) != DIT_OK) return st;
   dit_workspace_map m;
   build_map(dims, layout, 0, &m);
   if ((st = check_ws(ws, ws_bytes, m.total)) != DIT_OK) return st;
@@ -386,6 +435,8 @@ int loop_impl(const dit_dims* dims, const dit_layout* layout, const dit_block_we
     return fail(DIT_ERR_INVALID, "sigmas and temb_steps must be non-null");
   if (!x_latent) return fail(DIT_ERR_INVALID, "x_latent is null");
   if (((uintptr_t)x_latent) & 15) return fail(DIT_ERR_INVALID, "x_latent must be 16-byte aligned");
+  if ((st = check_aligned16(temb_steps, "temb_steps")) != DIT_OK) return st;
+  if ((st = check_block_spans(dims, layout->seq_pad, layout->seq_pad)) != DIT_OK) return st;
   if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
     return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
   for (int i = 0; i <= n_intervals && n_intervals > 0; ++i)
@@ -549,6 +600,7 @@ size_t dit_workspace_size_batched(const dit_dims* dims, const dit_layout* layout
   BlockRows br;
   dit_layout all;
   if (check_dims(dims) != DIT_OK || batch_rows(layouts, batch, &br, &all) != DIT_OK) return 0;
+  if (check_block_spans(dims, all.seq_pad, br.rows.seq_pad) != DIT_OK) return 0;
   dit_workspace_map m;
   build_map(dims, &all, 0, &m);
   if (map) *map = m;
@@ -569,6 +621,10 @@ int dit_block_forward_batched(const dit_dims* dims, const dit_layout* layouts, i
   if (!temb || !x_in || !x_out) return fail(DIT_ERR_INVALID, "temb, x_in and x_out must be non-null");
   if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
     return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
+  if ((st = check_aligned16(x_in, "x_in")) != DIT_OK) return st;
+  if ((st = check_aligned16(x_out, "x_out")) != DIT_OK) return st;
+  if ((st = check_aligned16(temb, "temb")) != DIT_OK) return st;
+  if ((st = check_block_spans(dims, all.seq_pad, br.rows.seq_pad)) != DIT_OK) return st;
   dit_workspace_map m;
   build_map(dims, &all, 0, &m);
   if ((st = check_ws(ws, ws_bytes, m.total)) != DIT_OK) return st;
@@ -610,6 +666,12 @@ int dit_attention_forward(const uint16_t* q, const uint16_t* k, const uint16_t* 
     return fail(DIT_ERR_INVALID, "batch strides must be multiples of 8");
   if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)o)) & 15)
     return fail(DIT_ERR_INVALID, "q, k, v and o must be 16-byte aligned");
+  if ((((uintptr_t)q_gain) | ((uintptr_t)k_gain)) & 15)
+    return fail(DIT_ERR_INVALID, "q_gain and k_gain must be 16-byte aligned");
+  {
+    const int st = check_span((int64_t)seq_pad * row_stride * 2, "one request's q/k/v rows");
+    if (st != DIT_OK) return st;
+  }
   if (attn_mode != DIT_ATTN_VALID_ONLY && attn_mode != DIT_ATTN_FIXED_VALID)
     return fail(DIT_ERR_INVALID, "attn_mode %d is not 0 (valid-only) or 1 (fixed-valid)", attn_mode);
   avdit::AttnArgs a{};
@@ -659,6 +721,15 @@ size_t head_ws_bytes(const dit_dims* d, const dit_layout* l, int32_t C) {
   return n < kAlign ? kAlign : n;
 }
 
+// The projection reads h [seq_pad, D] and one modality's weight [C, D] through 32-bit buffer
+// offsets.
+int check_head_spans(const dit_dims* d, const dit_layout* l, int32_t C) {
+  int st;
+  if ((st = check_span((int64_t)l->seq_pad * d->hidden * 2, "the head input rows [seq_pad, D]")) != DIT_OK)
+    return st;
+  return check_span((int64_t)C * d->hidden * 2, "one modality's output weight [C, D]");
+}
+
 int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_weights* hw,
               const float* temb, const void* x, float* v, void* ws, size_t ws_bytes,
               void* stream, bool f32) {
@@ -678,6 +749,10 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
   if (!temb || !x || !v) return fail(DIT_ERR_INVALID, "temb, x and v must be non-null");
   if ((((uintptr_t)x) & 15) || (((uintptr_t)v) & 15))
     return fail(DIT_ERR_INVALID, "x and v must be 16-byte aligned");
+  if ((st = check_aligned16(temb, "temb")) != DIT_OK) return st;
+  if ((st = check_aligned16(hw->norm_g, "norm_g")) != DIT_OK) return st;
+  if ((st = check_aligned16(hw->ada, "ada")) != DIT_OK) return st;
+  if ((st = check_head_spans(dims, layout, C)) != DIT_OK) return st;
   const size_t need = head_ws_bytes(dims, layout, C);
   if ((st = check_ws(ws, ws_bytes, need)) != DIT_OK) return st;
   const int32_t D = dims->hidden, L = layout->seq_pad;
@@ -738,6 +813,7 @@ size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout,
          out_channels, kMaxOutChannels);
     return 0;
   }
+  if (check_head_spans(dims, layout, out_channels) != DIT_OK) return 0;
   return head_ws_bytes(dims, layout, out_channels);
 }
 

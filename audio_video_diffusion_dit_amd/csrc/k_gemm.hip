@@ -524,6 +524,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.epilogue == EPI_BIAS_TO_F32 &&
       ((a.N & 3) != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 15) != 0))
     return hipErrorInvalidValue;
+  // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
+  const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
+  if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)total_rows(a.rows) * a.lda * 2 >= (int64_t)kOob)
+    return hipErrorInvalidValue;
   if (a.k_splits != 1) {
     // split reductions: fp32 partial outputs only, whole k-tiles per split, register-staged path
     if (a.k_splits < 1 || a.k_splits > 64 || a.epilogue != EPI_BIAS_TO_F32 || a.bias != nullptr ||
@@ -535,10 +539,6 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     return al ? gemm_instance<128, 128, 2, 2, EPI_BIAS_TO_F32, true>(a, s)
               : gemm_instance<128, 128, 2, 2, EPI_BIAS_TO_F32, false>(a, s);
   }
-  // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
-  const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
-  if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)total_rows(a.rows) * a.lda * 2 >= (int64_t)kOob)
-    return hipErrorInvalidValue;
   // a batch of requests: tiles of 256 (or 128) rows must not straddle two requests
   if (a.rows.batch > 1 && (a.rows.seq_pad % 256) != 0) return hipErrorInvalidValue;
   const bool aligned = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&

@@ -20,6 +20,17 @@
  *    stream. The library allocates no device memory and keeps no state between calls
  *    except a thread-local error string. Device work is enqueued asynchronously on the
  *    given stream (NULL = the default stream); calls return after enqueueing.
+ *  - Alignment: activations (x_in, x_out, latents, velocities), temb tables, and the fp32
+ *    parameters norm1_g, norm2_g, q_g, k_g, ada (and the head's norm_g, ada, bias) are read
+ *    or written with 16-byte vector accesses and must be 16-byte aligned (DIT_ERR_INVALID
+ *    otherwise). bf16 weight matrices may have any 2-byte alignment; unaligned ones take a
+ *    slower loader.
+ *  - Size limits: the kernels address their large operands through 32-bit byte offsets,
+ *    so each of these must span less than 2 GiB, else DIT_ERR_UNSUPPORTED: the weights
+ *    w_qkv, w_gate_up, w_down; the block activations [rows, D] and the SwiGLU activations
+ *    [rows, F] (rows = all rows of the call, batch * seq_pad for a batch); one request's
+ *    q/k/v rows [seq_pad, 3D] (at hidden 3072: seq_pad <= 116,508); the head's input
+ *    [seq_pad, D]. The workspace-size functions apply the same limits and return 0.
  *  - Errors: every argument is validated before anything is enqueued. On failure
  *    nothing is enqueued, a negative status is returned and dit_last_error() describes
  *    it. A launch failure reported by the runtime after enqueueing maps to

@@ -274,3 +274,94 @@ def test_head_workspace_and_validation(N):
     assert "out_channels" in (call(head=N.DitHeadWeights(256, 512, 1 << 24, None, 12)) and N.last_error())
     # an empty sequence validates and enqueues nothing
     assert call(layout=N.make_layout(0, 0, 0), nbytes=256) == N.DIT_OK
+
+
+def test_operand_spans_rejected_before_any_launch(N):
+    """Shapes whose operands would span 2 GiB or more (32-bit buffer offsets in the kernels) are
+    rejected with DIT_ERR_UNSUPPORTED during validation. The fake device addresses are never
+    dereferenced: on a machine without a GPU any launch would fail with DIT_ERR_DEVICE instead."""
+    d = N.make_dims(3072, 24, 128, 8192)
+    w = N.DitBlockWeights(*([256] * 9))
+    big = 1 << 40
+    # four 32,768-token requests at FFN 8192: the SwiGLU activations span 2^31 bytes
+    lays = [N.make_layout(30720, 2048, 32768)] * 4
+    arr = (N.DitLayout * 4)(*lays)
+    with pytest.raises(N.AvditError):      # size functions return 0 and set the message
+        N.dit_workspace_size_batched(d, lays)
+    assert "SwiGLU" in N.last_error() and "2 GiB" in N.last_error()
+    code = N.lib.dit_block_forward_batched(d, arr, 4, w, 256, 1 << 20, 1 << 36, 0, big, 1 << 38, None)
+    assert code == N.DIT_ERR_UNSUPPORTED and "SwiGLU" in N.last_error()
+    # one 131,072-token request
+    lay = N.make_layout(120000, 11072, 131072)
+    with pytest.raises(N.AvditError):
+        N.dit_workspace_size(d, lay, 0)
+    assert "2 GiB" in N.last_error()
+    code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 36, 0, big, 1 << 38, None)
+    assert code == N.DIT_ERR_UNSUPPORTED
+    # 116,509 rows: the first length whose q/k/v rows [seq_pad, 3D] reach 2 GiB at hidden 3072
+    lay = N.make_layout(116509, 0, 116509)
+    code = N.lib.dit_block_forward(d, lay, w, 256, 1 << 20, 1 << 36, 0, big, 1 << 38, None)
+    assert code == N.DIT_ERR_UNSUPPORTED and "q/k/v" in N.last_error()
+    n, _ = N.dit_workspace_size(d, N.make_layout(116508, 0, 116508), 0)
+    assert n > 0
+    # the same limits in the loop
+    blocks = (N.DitBlockWeights * 1)(w)
+    sig = (N.c_float * 2)(1.0, 0.0)
+    code = N.lib.denoise_loop(d, lay, blocks, 1, 1, sig, sig, 256, N.make_policy("off"), 1 << 20, 0,
+                              None, big, 1 << 38, None)
+    assert code == N.DIT_ERR_UNSUPPORTED
+    # attention alone: one request's rows reach 2 GiB
+    vl = (N.c_int32 * 1)(100000)
+    code = N.lib.dit_attention_forward(1 << 20, 1 << 21, 1 << 22, 1 << 23, 1, 116509, 24, 128, 0,
+                                       9216, 0, 3072, vl, None, None, 0, None)
+    assert code == N.DIT_ERR_UNSUPPORTED
+    # the velocity head: h [seq_pad, D] of 2 GiB
+    dh = N.make_dims(8192, 64, 128, 8192)
+    lay_h = N.make_layout(131072, 0, 131072)
+    with pytest.raises(N.AvditError):
+        N.dit_head_workspace_size(dh, lay_h, 128)
+    assert "2 GiB" in N.last_error()
+    head = N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 128)
+    code = N.lib.dit_velocity_head(dh, lay_h, head, 1 << 20, 1 << 36, 1 << 37, big, 1 << 38, None)
+    assert code == N.DIT_ERR_UNSUPPORTED
+
+
+def test_vector_accessed_pointers_must_be_aligned(N):
+    """Every pointer the kernels access with 16-byte vectors is checked before any launch."""
+    d = N.make_dims(256, 4, 64, 683)
+    lay = N.make_layout(512, 96, 640)
+    need, _ = N.dit_workspace_size(d, lay, 0)
+    big = 1 << 40
+    good = [256] * 9
+    f = N.lib.dit_block_forward
+    for i in range(4, 9):     # norm1_g, norm2_g, q_g, k_g, ada
+        bad = list(good)
+        bad[i] = 256 + 8
+        code = f(d, lay, N.DitBlockWeights(*bad), 256, 1 << 20, 1 << 30, 0, big, need, None)
+        assert code == N.DIT_ERR_INVALID and "aligned" in N.last_error(), i
+    assert f(d, lay, N.DitBlockWeights(*good), 256 + 4, 1 << 20, 1 << 30, 0, big, need, None) == N.DIT_ERR_INVALID
+    assert f(d, lay, N.DitBlockWeights(*good), 256, (1 << 20) + 8, 1 << 30, 0, big, need, None) == N.DIT_ERR_INVALID
+    assert f(d, lay, N.DitBlockWeights(*good), 256, 1 << 20, (1 << 30) + 2, 0, big, need, None) == N.DIT_ERR_INVALID
+    # the batched block and the loop check the same pointers
+    arr = (N.DitLayout * 1)(lay)
+    assert N.lib.dit_block_forward_batched(d, arr, 1, N.DitBlockWeights(*good), 256, (1 << 20) + 8,
+                                           1 << 30, 0, big, need, None) == N.DIT_ERR_INVALID
+    bad = list(good)
+    bad[8] = 256 + 4
+    blocks = (N.DitBlockWeights * 2)(N.DitBlockWeights(*good), N.DitBlockWeights(*bad))
+    sig = (N.c_float * 2)(1.0, 0.0)
+    need_l, _ = N.dit_workspace_size(d, lay, 2)
+    code = N.lib.denoise_loop(d, lay, blocks, 2, 1, sig, sig, 256, N.make_policy("off"), 1 << 20, 0,
+                              None, big, need_l, None)
+    assert code == N.DIT_ERR_INVALID and "block 1" in N.last_error()
+    code = N.lib.denoise_loop(d, lay, (N.DitBlockWeights * 1)(N.DitBlockWeights(*good)), 1, 1, sig,
+                              sig, 256 + 8, N.make_policy("off"), 1 << 20, 0, None, big, need_l, None)
+    assert code == N.DIT_ERR_INVALID
+    # the head's norm gain, table and temb
+    need_h = N.dit_head_workspace_size(d, lay, 64)
+    g = N.lib.dit_velocity_head
+    for head in (N.DitHeadWeights(256 + 4, 512, 1 << 24, 1 << 25, 64),
+                 N.DitHeadWeights(256, 512 + 8, 1 << 24, 1 << 25, 64)):
+        assert g(d, lay, head, 1 << 20, 1 << 32, 1 << 34, 1 << 30, need_h, None) == N.DIT_ERR_INVALID
+    head = N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 64)
+    assert g(d, lay, head, (1 << 20) + 4, 1 << 32, 1 << 34, 1 << 30, need_h, None) == N.DIT_ERR_INVALID
