@@ -567,12 +567,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (aligned) {
-    // 256 x 256 tiles over 8 waves (two per SIMD, 128 x 64 accumulators each) measured faster
-    // than 4 waves of 128 x 128 at every projection of the 32k-token block.
-    if (big) return gemm_dispatch_epi<256, 256, 2, 4, true>(a, s);
-    return gemm_dispatch_epi<128, 128, 2, 2, true>(a, s);
-  }
+  // small problems, reductions that are not a multiple of 64, and unaligned operands
+  if (aligned) return gemm_dispatch_epi<128, 128, 2, 2, true>(a, s);
   return gemm_dispatch_epi<128, 128, 2, 2, false>(a, s);
 }
 

@@ -12,8 +12,11 @@ timed too, for steps/sec off vs conservative.
 roofline: the attention kernel (the largest FLOP share of the block at this length), timed
 with HIP events on the stream it runs on over repeated launches on the block's own q/k/v
 layout; useful FLOPs 4 V^2 D per launch against the 2.5 PFLOP/s dense bf16 MFMA peak.
-cpu_baseline: the float64 oracle on the host cores, one block of the same workload with a
-sample of output rows (keys/values for every valid row), in the same useful-FLOP unit.
+cpu_baseline: the oracle on the host cores, one block of the same workload with a sample of
+output rows (keys/values for every valid row), in the same useful-FLOP unit, evaluated in float32
+(the figure) and in float64 (beside it).
+quality_conservative_vs_off: cosine, relative L2 and PSNR between the final latents of the
+conservative and the cache-off loop (report only).
 roofline.traffic: HBM bytes per attention launch from the committed counter summary
 profiles/k_attn_traffic.json (FETCH_SIZE and WRITE_SIZE, scaled by the same counters on a
 1 GiB device copy), reported only while that summary's recorded source hash matches the
@@ -79,32 +82,37 @@ def log(msg):
 
 
 def cpu_baseline(case, rows_n):
-    """Float64 oracle on the host cores: one block of the workload, rows_n sampled output rows."""
+    """The oracle on the host cores: one block of the workload, rows_n sampled output rows (keys
+    and values for every valid row), evaluated in float32 (the baseline figure) and in float64
+    (the precision the oracle checks in)."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    from audio_video_diffusion_dit_amd.inputs import bf16_bits, bf16_to_f32
+    threads = _blas_threads()
     wl = case.wl
     V, D, F = wl.n_valid, wl.hidden, wl.ffn
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(V, rows_n, replace=False))
-    blk = {k: np.asarray(v, dtype=np.float64) for k, v in case.blocks[0].as_float().items()}
-    from audio_video_diffusion_dit_amd.inputs import bf16_bits, bf16_to_f32
-    x = bf16_to_f32(bf16_bits(case.x0)).astype(np.float64)
     dims = O.Dims(D, wl.heads, wl.head_dim, F)
     lay = O.Layout(wl.n_video, wl.n_audio, wl.seq_pad)
-    t0 = time.perf_counter()
-    O.block_forward(x, blk, case.temb_steps[0], dims, lay, rows=rows)
-    dt = time.perf_counter() - t0
     R = float(rows_n)
     flops = 4.0 * V * D * D + R * (4.0 * D * D + 6.0 * D * F + 4.0 * V * D)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"one block of {wl.name} (float64 NumPy): keys/values for all {V} valid rows, "
-                      f"{rows_n} sampled output rows; {flops:.3e} useful FLOPs"}
+    secs = {}
+    for dt in (np.float32, np.float64):
+        blk = {k: np.asarray(v, dtype=dt) for k, v in case.blocks[0].as_float().items()}
+        x = bf16_to_f32(bf16_bits(case.x0)).astype(dt)
+        temb = np.asarray(case.temb_steps[0], dtype=dt)
+        with O.precision(dt):
+            t0 = time.perf_counter()
+            O.block_forward(x, blk, temb, dims, lay, rows=rows)
+            secs[np.dtype(dt).name] = time.perf_counter() - t0
+    t32, t64 = secs["float32"], secs["float64"]
+    return {"value": flops / t32 / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(t32, 3),
+            "float64": {"value": flops / t64 / 1e12, "seconds": round(t64, 3)},
+            "sample": f"one block of {wl.name} evaluated by the oracle in float32 (float64 beside "
+                      f"it): keys/values for all {V} valid rows, {rows_n} sampled output rows; "
+                      f"{flops:.3e} useful FLOPs"}
 
 
 def _blas_threads():
@@ -113,6 +121,20 @@ def _blas_threads():
         return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         return os.cpu_count()
+
+
+def latent_compare(a, ref):
+    """Conservative-vs-off comparison of two final latents (report only): cosine, relative L2
+    |a - ref| / |ref|, and PSNR 10 log10(peak^2 / MSE) with the peak max |ref|."""
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    d = a - ref
+    mse = float(np.mean(d * d))
+    peak = float(np.max(np.abs(ref)))
+    return {"cosine": round(float(a @ ref / (np.linalg.norm(a) * np.linalg.norm(ref))), 7),
+            "rel_l2": float(f"{np.linalg.norm(d) / np.linalg.norm(ref):.4e}"),
+            "psnr_db": round(10.0 * np.log10(peak * peak / mse), 2) if mse > 0 else None}
 
 
 def configs_report(args):
@@ -384,7 +406,7 @@ def main():
         4.0 * float(wl.n_valid) ** 2 * wl.hidden
 
     t_c = t_o = flops_c = flops_o = None
-    calls = hits = None
+    calls = hits = quality = None
     if not args.roofline_only:
         ws, _ = dev.workspace(dims, lay, len(blocks))
         pol_c = N.make_policy("conservative")
@@ -410,6 +432,7 @@ def main():
         assert abs(flops_c - st.executed_blocks * per_block) <= 1e-6 * flops_c
         calls, hits = st.dit_calls, st.cache_hits
         log(f"[bench] conservative: {t_c:.3f} s/loop, {flops_c / t_c / 1e12:.1f} TFLOP/s")
+        x_cons = x[: wl.n_valid].cpu().numpy()
         if not args.no_off:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
@@ -418,6 +441,9 @@ def main():
             t_o = time.perf_counter() - t0
             flops_o = so.useful_flops
             log(f"[bench] off: {t_o:.3f} s/loop, {flops_o / t_o / 1e12:.1f} TFLOP/s")
+            quality = latent_compare(x_cons, x[: wl.n_valid].cpu().numpy())
+            quality["over"] = "final latents, all valid rows (conservative vs cache off)"
+            log(f"[bench] conservative vs off: {quality}")
         del ws
 
     # roofline: the attention kernel on the block's own qkv layout (filled by one block call)
@@ -480,6 +506,7 @@ def main():
         "tflops_off": round(flops_o / t_o / 1e12, 2) if t_o else None,
         "dit_calls": calls,
         "cache_hits": hits,
+        "quality_conservative_vs_off": quality,
         "roofline": {"kernel": "avdit::k_attn<128> (valid-only attention, 4 V^2 D flop/launch)",
                      "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

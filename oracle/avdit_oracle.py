@@ -31,12 +31,34 @@ against scalar loops that round each stored element.
 from __future__ import annotations
 
 import math
+from contextlib import contextmanager
 from dataclasses import dataclass
 from typing import Callable, Optional, Sequence
 
 import numpy as np
 
 F64 = np.float64
+
+_WORK_DTYPE = [F64]
+
+
+def work_dtype():
+    """Floating type of the block arithmetic: float64, unless a ``precision`` block says
+    otherwise."""
+    return _WORK_DTYPE[0]
+
+
+@contextmanager
+def precision(dtype):
+    """Evaluate the layout, norm, projection, RoPE, attention and SwiGLU functions (and so
+    ``block_forward``) in another floating type: the same definitions at that precision. The
+    checker is always float64; float32 is used only to time a single-precision evaluation."""
+    prev = _WORK_DTYPE[0]
+    _WORK_DTYPE[0] = np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _WORK_DTYPE[0] = prev
 
 # Order of the six AdaLN modulation rows of one modality.
 SHIFT_MSA, SCALE_MSA, GATE_MSA, SHIFT_MLP, SCALE_MLP, GATE_MLP = range(6)
@@ -94,8 +116,8 @@ def row_modality(layout: Layout) -> np.ndarray:
 def row_positions(layout: Layout, positions: Optional[np.ndarray] = None) -> np.ndarray:
     """Rotary position of every row: the packed index unless an array is given."""
     if positions is None:
-        return np.arange(layout.seq_pad, dtype=F64)
-    return np.asarray(positions, dtype=F64)
+        return np.arange(layout.seq_pad, dtype=work_dtype())
+    return np.asarray(positions, dtype=work_dtype())
 
 
 # --------------------------------------------------------- elementwise ops --
@@ -119,14 +141,14 @@ def bf16_round(a) -> np.ndarray:
 
 def rms_normalize(x: np.ndarray, eps: float) -> np.ndarray:
     """x / sqrt(mean(x^2) + eps) over the last axis (RMSNorm without its gain)."""
-    x = np.asarray(x, dtype=F64)
+    x = np.asarray(x, dtype=work_dtype())
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps)
 
 
 def silu(u: np.ndarray) -> np.ndarray:
     """u * sigmoid(u) = u / (1 + exp(-u))."""
-    u = np.asarray(u, dtype=F64)
+    u = np.asarray(u, dtype=work_dtype())
     return u / (1.0 + np.exp(-u))
 
 
@@ -141,7 +163,7 @@ def modulation_rows(ada: np.ndarray, temb: np.ndarray) -> np.ndarray:
     timestep embedding T have one [6, D] slice per modality, and a row picks its
     slice by modality id.
     """
-    return np.asarray(ada, dtype=F64) + np.asarray(temb, dtype=F64)
+    return np.asarray(ada, dtype=work_dtype()) + np.asarray(temb, dtype=work_dtype())
 
 
 def norm_modulate(x, gain, E, modality, shift_chunk: int, scale_chunk: int, eps: float):
@@ -149,12 +171,12 @@ def norm_modulate(x, gain, E, modality, shift_chunk: int, scale_chunk: int, eps:
 
     [P1 §2] fused RMSNorm + indexed AdaLN; [P3 "Changes Made"] indexed modulation.
     """
-    x = np.asarray(x, dtype=F64)
+    x = np.asarray(x, dtype=work_dtype())
     out = np.zeros_like(x)
     valid = modality >= 0
     if not valid.any():
         return out
-    xn = rms_normalize(x[valid], eps) * np.asarray(gain, dtype=F64)
+    xn = rms_normalize(x[valid], eps) * np.asarray(gain, dtype=work_dtype())
     Em = E[modality[valid]]  # [V, 6, D]
     out[valid] = xn * (1.0 + Em[:, scale_chunk]) + Em[:, shift_chunk]
     return out
@@ -164,7 +186,7 @@ def norm_modulate(x, gain, E, modality, shift_chunk: int, scale_chunk: int, eps:
 
 def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     """x @ w^T with w in [out, in] layout, no bias."""
-    return np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+    return np.asarray(x, dtype=work_dtype()) @ np.asarray(w, dtype=work_dtype()).T
 
 
 def qk_rms_norm(t: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
@@ -173,13 +195,13 @@ def qk_rms_norm(t: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     [P1 §2] and [P3 "Changes Made"]: Q/K RMSNorm before RoPE. Read as a per-head
     norm (gain of length head_dim).
     """
-    return rms_normalize(t, eps) * np.asarray(gain, dtype=F64)
+    return rms_normalize(t, eps) * np.asarray(gain, dtype=work_dtype())
 
 
 def rope_inv_freq(head_dim: int, base: float) -> np.ndarray:
     """inv_i = base^(-2i / head_dim), i = 0 .. head_dim/2 - 1."""
     i = np.arange(head_dim // 2, dtype=F64)
-    return np.power(F64(base), -2.0 * i / head_dim)
+    return np.power(F64(base), -2.0 * i / head_dim).astype(work_dtype())
 
 
 def rope_neox(t: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
@@ -190,9 +212,9 @@ def rope_neox(t: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
       out[i]        = t[i] cos - t[i+Dh/2] sin
       out[i+Dh/2]   = t[i+Dh/2] cos + t[i] sin
     """
-    t = np.asarray(t, dtype=F64)
+    t = np.asarray(t, dtype=work_dtype())
     half = t.shape[-1] // 2
-    theta = np.asarray(pos, dtype=F64)[:, None] * rope_inv_freq(t.shape[-1], base)[None, :]
+    theta = np.asarray(pos, dtype=work_dtype())[:, None] * rope_inv_freq(t.shape[-1], base)[None, :]
     c = np.cos(theta)[:, None, :]
     s = np.sin(theta)[:, None, :]
     a, b = t[..., :half], t[..., half:]
@@ -211,14 +233,14 @@ def attention_valid(q, k, v, n_valid: int, p_store: Optional[Callable] = None) -
     probabilities before they weight the values and are summed, i.e. the form in
     which they are stored as the operand of the P.V product.
     """
-    q = np.asarray(q, dtype=F64)
+    q = np.asarray(q, dtype=work_dtype())
     L, H, Dh = q.shape
-    out = np.zeros((L, H, Dh), dtype=F64)
+    out = np.zeros((L, H, Dh), dtype=work_dtype())
     if n_valid == 0:
         return out
     qv = q[:n_valid].transpose(1, 0, 2)                           # [H, V, Dh]
-    kv = np.asarray(k, dtype=F64)[:n_valid].transpose(1, 0, 2)
-    vv = np.asarray(v, dtype=F64)[:n_valid].transpose(1, 0, 2)
+    kv = np.asarray(k, dtype=work_dtype())[:n_valid].transpose(1, 0, 2)
+    vv = np.asarray(v, dtype=work_dtype())[:n_valid].transpose(1, 0, 2)
     s = (qv @ kv.transpose(0, 2, 1)) / math.sqrt(Dh)               # [H, V, V]
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
@@ -233,10 +255,10 @@ def attention_rows(q_rows, k, v, n_valid: int, p_store: Optional[Callable] = Non
     """Attention output for a subset of query rows q_rows [R, H, Dh] against the
     valid keys k[:n_valid], v[:n_valid] (same definition as ``attention_valid``,
     p_store likewise)."""
-    q_rows = np.asarray(q_rows, dtype=F64)
+    q_rows = np.asarray(q_rows, dtype=work_dtype())
     Dh = q_rows.shape[-1]
-    kv = np.asarray(k, dtype=F64)[:n_valid].transpose(1, 0, 2)     # [H, V, Dh]
-    vv = np.asarray(v, dtype=F64)[:n_valid].transpose(1, 0, 2)
+    kv = np.asarray(k, dtype=work_dtype())[:n_valid].transpose(1, 0, 2)     # [H, V, Dh]
+    vv = np.asarray(v, dtype=work_dtype())[:n_valid].transpose(1, 0, 2)
     qr = q_rows.transpose(1, 0, 2)                                 # [H, R, Dh]
     s = (qr @ kv.transpose(0, 2, 1)) / math.sqrt(Dh)
     s = s - s.max(axis=-1, keepdims=True)
@@ -252,7 +274,7 @@ def swiglu(h, w_gate_up, ffn: int) -> np.ndarray:
 
     [P3 "Changes Made"]: fused SwiGLU. Gate rows come first in the packed weight.
     """
-    w = np.asarray(w_gate_up, dtype=F64)
+    w = np.asarray(w_gate_up, dtype=work_dtype())
     g = linear(h, w[:ffn])
     u = linear(h, w[ffn:2 * ffn])
     return silu(g) * u
@@ -290,7 +312,7 @@ def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
     """
     st = store if store is not None else (lambda name, a: a)
     D, H, Dh, F = dims.hidden, dims.heads, dims.head_dim, dims.ffn
-    x = np.asarray(x, dtype=F64)
+    x = np.asarray(x, dtype=work_dtype())
     L = layout.seq_pad
     V = layout.n_valid
     mod = row_modality(layout)
@@ -298,7 +320,7 @@ def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
     E = modulation_rows(blk["ada"], temb)
 
     h = st("h", norm_modulate(x, blk["norm1_g"], E, mod, SHIFT_MSA, SCALE_MSA, dims.norm_eps))
-    w_qkv = np.asarray(blk["w_qkv"], dtype=F64)
+    w_qkv = np.asarray(blk["w_qkv"], dtype=work_dtype())
     kv_rows = slice(0, V)
     k = st("qkv", linear(h[kv_rows], w_qkv[D:2 * D])).reshape(V, H, Dh)
     v = st("qkv", linear(h[kv_rows], w_qkv[2 * D:3 * D])).reshape(V, H, Dh)
@@ -320,13 +342,13 @@ def block_forward(x, blk: dict, temb, dims: Dims, layout: Layout,
     Es = E[ms]                                              # [R, 6, D]
     y = linear(o, blk["w_o"])
     x1 = st("x1", x[sel_valid] + Es[:, GATE_MSA] * y)
-    x1n = rms_normalize(x1, dims.norm_eps) * np.asarray(blk["norm2_g"], dtype=F64)
+    x1n = rms_normalize(x1, dims.norm_eps) * np.asarray(blk["norm2_g"], dtype=work_dtype())
     h2 = st("h2", x1n * (1.0 + Es[:, SCALE_MLP]) + Es[:, SHIFT_MLP])
     a = st("act", swiglu(h2, blk["w_gate_up"], F))
     z = linear(a, blk["w_down"])
     x2_sel = st("out", x1 + Es[:, GATE_MLP] * z)
 
-    out = np.zeros((len(rows), D), dtype=F64)
+    out = np.zeros((len(rows), D), dtype=work_dtype())
     idx = np.nonzero(rows < V)[0]
     out[idx] = x2_sel
     if not want_intermediates:

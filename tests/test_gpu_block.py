@@ -207,3 +207,28 @@ def test_block_attention_softmax_paths(env, name, gain, path):
     o_ref = O.attention_valid(q_g, k_g, v_g, V).reshape(V, D)
     assert_kernel_close(it["o"][:V], o_ref, f"attention ({path} softmax path)")
     assert np.all(it["o"][V:] == 0)
+
+
+def test_block_32k_sampled_rows(env):
+    """One block at the benchmarked 32,768-token shape (30,720 video + 2,048 audio, no tail;
+    D=3072, 24 x 128 heads, F=8192): rows 0, 30719, 30720, 32767 (both ends of both modalities,
+    the largest rotary positions) and 60 drawn rows against the oracle, which computes keys and
+    values for all 32,768 rows; fixed-valid equals valid-only bit for bit."""
+    N, dev = env
+    from audio_video_diffusion_dit_amd import inputs as I
+    wl = I.WORKLOADS["loop_8blk_32k"]
+    case = I.block_case(wl, seed=0, n_blocks=1)
+    V = wl.n_valid
+    say(f"block 32k sampled rows: V={V} L={wl.seq_pad} D={wl.hidden} F={wl.ffn}")
+    out, _, _ = _gpu_block(env, case)
+    bits = dev.bf16_bits_of(out)
+    fv, _, _ = _gpu_block(env, case, attn_mode=N.DIT_ATTN_FIXED_VALID)
+    assert np.array_equal(bits, dev.bf16_bits_of(fv)), "fixed-valid and valid-only differ"
+    got = dev.bf16_values_of(out).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(32)
+    edges = [0, wl.n_video - 1, wl.n_video, V - 1]
+    rows = np.sort(np.concatenate([rng.choice(np.setdiff1d(np.arange(V), edges), 60, replace=False),
+                                   edges]))
+    check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl,
+                "32k block sampled rows", rows=rows)

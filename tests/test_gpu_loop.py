@@ -164,3 +164,52 @@ def test_loop_4blk_schedule_and_teacher_forced_blocks(env):
                                    [0, wl.n_video - 1, wl.n_video, V - 1]]))
     comp = _composed(env, case, hits, check_steps=(0, 11), rows=rows)
     assert np.array_equal(comp, got), "loop != composed block/step calls"
+
+
+def _latent_compare(a, ref):
+    a = np.asarray(a, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    d = a - ref
+    mse = float(np.mean(d * d))
+    peak = float(np.max(np.abs(ref)))
+    return dict(cosine=float(a @ ref / (np.linalg.norm(a) * np.linalg.norm(ref))),
+                rel_l2=float(np.linalg.norm(d) / np.linalg.norm(ref)),
+                psnr_db=float(10.0 * np.log10(peak * peak / mse)) if mse > 0 else float("inf"))
+
+
+def test_loop_4blk_free_running_vs_golden(env):
+    """The 4-block, 4,608-token, 49-interval loop run free on the GPU, cache off and
+    conservative, against the float64 oracle's final latents (sampled rows written by
+    tests/golden/make_loop_4blk_golden.py, oracle only): the stated bar on the fp32 latent, the
+    hit flags bit for bit. The conservative-vs-off comparison of the GPU's own final latents is
+    reported beside the oracle's (report only)."""
+    import json
+    import os
+    import oracle as O
+    from audio_video_diffusion_dit_amd import inputs as I
+    with open(os.path.join(os.path.dirname(__file__), "golden", "loop_4blk_final_rows.json")) as f:
+        gold = json.load(f)
+    wl = I.WORKLOADS["loop_4blk"]
+    g = gold["workload"]
+    assert (g["hidden"], g["heads"], g["ffn"], g["n_video"], g["n_audio"], g["n_blocks"],
+            g["n_intervals"]) == (wl.hidden, wl.heads, wl.ffn, wl.n_video, wl.n_audio,
+                                  wl.n_blocks, wl.n_intervals)
+    case = I.loop_case(wl, seed=g["seed"])
+    rows = np.asarray(gold["rows"])
+    V = wl.n_valid
+    finals = {}
+    for mode, key in (("off", "final_off"), ("conservative", "final_conservative")):
+        say(f"loop_4blk free running ({mode}): 4 blocks, 49 intervals, V={V}")
+        got, stats, hits = _gpu_loop(env, case, mode)
+        want_hits = gold["hits_conservative"] if mode == "conservative" else gold["hits_off"]
+        assert [int(h) for h in hits] == want_hits
+        assert hits == O.cache_schedule(O.CachePolicy(mode=mode), 49)
+        assert np.all(got[V:] == 0)
+        assert_close(got[rows], np.asarray(gold[key]), f"final latent, sampled rows ({mode})")
+        finals[mode] = got[:V]
+    gpu_q = _latent_compare(finals["conservative"], finals["off"])
+    ref_q = gold["conservative_vs_off_all_valid_rows"]
+    say(f"  conservative vs off, all valid rows: GPU cos {gpu_q['cosine']:.6f} rel-L2 "
+        f"{gpu_q['rel_l2']:.4e} PSNR {gpu_q['psnr_db']:.2f} dB; oracle cos {ref_q['cosine']:.6f} "
+        f"rel-L2 {ref_q['rel_l2']:.4e} PSNR {ref_q['psnr_db']:.2f} dB")
+    assert np.isfinite(gpu_q["rel_l2"])
