@@ -24,7 +24,10 @@ EXPORTED = ("dit_last_error", "dit_version", "dit_cache_schedule", "dit_workspac
             "dit_block_forward", "dit_block_forward_f32", "dit_block_forward_batched",
             "dit_workspace_size_batched", "step_update", "denoise_loop", "denoise_loop_f32",
             "dit_attention_forward", "dit_head_workspace_size", "dit_velocity_head",
-            "dit_velocity_head_f32")
+            "dit_velocity_head_f32", "dit_block_forward_noalloc")
+
+# Bytes of the built-in scratch of dit_block_forward_noalloc (DIT_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class DitDims(ctypes.Structure):
@@ -97,6 +100,10 @@ def _load():
     lib.dit_block_forward_batched.argtypes = [POINTER(DitDims), POINTER(DitLayout), c_int32,
                                               POINTER(DitBlockWeights), c_void_p, c_void_p,
                                               c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
+    lib.dit_block_forward_noalloc.restype = c_int32
+    lib.dit_block_forward_noalloc.argtypes = [POINTER(DitDims), POINTER(DitLayout),
+                                              POINTER(DitBlockWeights), c_void_p, c_void_p,
+                                              c_void_p, c_int32, c_void_p]
     lib.dit_block_forward_f32.restype = c_int32
     lib.dit_block_forward_f32.argtypes = lib.dit_block_forward.argtypes
     lib.dit_head_workspace_size.restype = c_size_t
@@ -215,6 +222,14 @@ def dit_block_forward(dims, layout, weights: DitBlockWeights, temb, x_in, x_out,
     _check(lib.dit_block_forward(ctypes.byref(dims), ctypes.byref(layout), ctypes.byref(weights),
                                  _ptr(temb), _ptr(x_in), _ptr(x_out), attn_mode, _ptr(ws), ws_bytes,
                                  _stream(stream)), "dit_block_forward")
+
+
+def dit_block_forward_noalloc(dims, layout, weights: DitBlockWeights, temb, x_in, x_out,
+                              attn_mode=DIT_ATTN_VALID_ONLY, stream=None):
+    """dit_block_forward on the library's built-in scratch: no workspace argument."""
+    _check(lib.dit_block_forward_noalloc(ctypes.byref(dims), ctypes.byref(layout),
+                                         ctypes.byref(weights), _ptr(temb), _ptr(x_in), _ptr(x_out),
+                                         attn_mode, _stream(stream)), "dit_block_forward_noalloc")
 
 
 def dit_workspace_size_batched(dims: DitDims, layouts):

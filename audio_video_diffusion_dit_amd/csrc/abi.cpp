@@ -28,6 +28,15 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+int avdit::set_last_error(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
+namespace {
+
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxSeq = 1 << 20;
 constexpr int32_t kMaxHidden = 8192;

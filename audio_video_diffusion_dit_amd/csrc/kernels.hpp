@@ -165,4 +165,8 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// Sets the calling thread's dit_last_error() message and returns code (host code of the
+// library's entry points outside abi.cpp).
+int set_last_error(int code, const char* msg);
+
 }  // namespace avdit

@@ -186,6 +186,23 @@ int dit_block_forward(const dit_dims* dims, const dit_layout* layout,
                       const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* dit_block_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The block's intermediates live in a device array built into the library, one
+ * copy per GPU of DIT_NOALLOC_SCRATCH_BYTES (128 MiB), held from the first call on that GPU
+ * (its address is looked up once per device, on the device current at the call) until the
+ * process ends. The call allocates nothing and runs the same kernels as dit_block_forward,
+ * with the same result bit for bit. A block whose dit_workspace_size(dims, layout, 0) exceeds
+ * DIT_NOALLOC_SCRATCH_BYTES is rejected with DIT_ERR_UNSUPPORTED before any device call.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. Other arguments, errors
+ * and aliasing rules as dit_block_forward; a failed scratch lookup is DIT_ERR_DEVICE. */
+#define DIT_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int dit_block_forward_noalloc(const dit_dims* dims, const dit_layout* layout,
+                              const dit_block_weights* weights, const float* temb,
+                              const uint16_t* x_in, uint16_t* x_out, int32_t attn_mode,
+                              void* stream);
+
 /* Workspace for dit_block_forward_batched: the workspace of one block over all batch * seq_pad
  * rows, and its map. Returns 0 with dit_last_error() set for invalid dims or layouts. */
 size_t dit_workspace_size_batched(const dit_dims* dims, const dit_layout* layouts, int32_t batch,

@@ -365,3 +365,25 @@ def test_vector_accessed_pointers_must_be_aligned(N):
         assert g(d, lay, head, 1 << 20, 1 << 32, 1 << 34, 1 << 30, need_h, None) == N.DIT_ERR_INVALID
     head = N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 64)
     assert g(d, lay, head, (1 << 20) + 4, 1 << 32, 1 << 34, 1 << 30, need_h, None) == N.DIT_ERR_INVALID
+
+
+def test_noalloc_entry_point_rejects_oversize_blocks_before_device_work(N):
+    """The no-allocation block entry point takes blocks whose workspace fits its built-in
+    128 MiB scratch; larger ones are rejected with DIT_ERR_UNSUPPORTED before any device call
+    (on this GPU-less machine a device call would give DIT_ERR_DEVICE); invalid dims get
+    dit_block_forward's own status."""
+    w = N.DitBlockWeights(*([256] * 9))
+    d = N.make_dims(3072, 24, 128, 8192)
+    lay = N.make_layout(30720, 2048, 32768)
+    code = N.lib.dit_block_forward_noalloc(d, lay, w, 256, 1 << 20, 1 << 36, 0, None)
+    assert code == N.DIT_ERR_UNSUPPORTED and "scratch" in N.last_error()
+    d2 = N.make_dims(1024, 8, 128, 2816)
+    n, _ = N.dit_workspace_size(d2, N.make_layout(4096, 512, 4608), 0)
+    assert n <= N.NOALLOC_SCRATCH_BYTES          # the 4,608-token loop block fits
+    bad = N.make_dims(256, 4, 96, 683)
+    code = N.lib.dit_block_forward_noalloc(bad, N.make_layout(10, 0, 16), w, 256, 1 << 20, 1 << 30,
+                                           0, None)
+    assert code == N.DIT_ERR_UNSUPPORTED and "head_dim" in N.last_error()
+    code = N.lib.dit_block_forward_noalloc(N.make_dims(256, 4, 64, 683), N.make_layout(20, 0, 16),
+                                           w, 256, 1 << 20, 1 << 30, 0, None)
+    assert code == N.DIT_ERR_INVALID
