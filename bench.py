@@ -22,8 +22,9 @@ profiles/k_attn_traffic.json (FETCH_SIZE and WRITE_SIZE, scaled by the same coun
 1 GiB device copy), reported only while that summary's recorded source hash matches the
 current attention kernel source; otherwise null.
 
-Prints ONE JSON line. --roofline-only runs just one block, the attention timing and the copy
-used to calibrate the traffic counters (the command the counter runs profile).
+Prints ONE JSON line. --roofline-only runs just one block, the attention timing, two Euler
+steps and the copy used to calibrate the traffic counters (the command the counter runs
+profile). --configs prints the per-workload report instead (--only selects workloads).
 """
 
 import argparse
@@ -55,6 +56,10 @@ def parse():
     p.add_argument("--configs", action="store_true",
                    help="per-workload report instead of the bench line: GPU and float64-oracle "
                         "timings of every configuration, one JSON line each")
+    p.add_argument("--only", default=None,
+                   help="with --configs: comma-separated subset of block_small, loop_4blk, "
+                        "block_h3, loop_8blk_32k, loop_4blk_loop, block_ragged, head_32k, "
+                        "attn_ragged, attn_ragged_qknorm")
     return p.parse_args()
 
 
@@ -138,14 +143,15 @@ def latent_compare(a, ref):
 
 
 def configs_report(args):
-    """GPU and float64-oracle timings of every workload, one JSON line per measurement.
+    """GPU and oracle timings of every workload, one JSON line per measurement.
 
     GPU: 3 warm-up calls, then the median of 10 single-call timings with HIP events on the
     stream (loops: median of 3). Useful FLOPs count valid tokens only (8VD^2 + 6VDF + 4V^2D per
-    block; attention 4 v^2 H Dh per request). Oracle: the float64 NumPy implementation on the
-    host cores, on the whole block where that takes seconds, else on a sample of output rows
-    (keys and values for every valid row), in the same useful-FLOP unit; the 4-block loop's
-    oracle time is extrapolated from one full block and labelled so.
+    block; attention 4 v^2 H Dh per request). Oracle (unless --no-cpu-baseline): the float64
+    NumPy implementation on the host cores, on the whole block where that takes seconds, else on
+    a sample of output rows (keys and values for every valid row), in the same useful-FLOP unit;
+    the 4-block loop's oracle time is extrapolated from one full block and labelled so.
+    --only restricts the report to the named workloads (for kernel traces of one of them).
     """
     import statistics
     import numpy as np
@@ -161,6 +167,11 @@ def configs_report(args):
             "oracle_threads": int(_blas_threads()), "host_cores": len(os.sched_getaffinity(0))}
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    only = set(args.only.split(",")) if args.only else None
+    run_oracle = not args.no_cpu_baseline
+
+    def want(name):
+        return only is None or name in only
 
     def gpu_ms(fn, warm=3, reps=10):
         for _ in range(warm):
@@ -182,6 +193,8 @@ def configs_report(args):
         return 8.0 * V * D * D + 6.0 * V * D * F + 4.0 * float(V) ** 2 * D
 
     def oracle_block(case, rows_n):
+        if not run_oracle:
+            return None
         wl = case.wl
         V, D, F = wl.n_valid, wl.hidden, wl.ffn
         blk = {k: np.asarray(v, dtype=np.float64) for k, v in case.blocks[0].as_float().items()}
@@ -192,19 +205,18 @@ def configs_report(args):
             t0 = time.perf_counter()
             O.block_forward(x, blk, case.temb, dims, lay)
             dt = time.perf_counter() - t0
-            return {"seconds": round(dt, 3), "value": block_flops(V, D, F) / dt / 1e12,
+            return {"seconds": round(dt, 3), "value": round(block_flops(V, D, F) / dt / 1e12, 5),
                     "unit": "TFLOP/s", "sample": "whole block"}
         rows = np.sort(np.random.default_rng(0).choice(V, rows_n, replace=False))
         t0 = time.perf_counter()
         O.block_forward(x, blk, case.temb, dims, lay, rows=rows)
         dt = time.perf_counter() - t0
         fl = 4.0 * V * D * D + rows_n * (4.0 * D * D + 6.0 * D * F + 4.0 * V * D)
-        return {"seconds": round(dt, 3), "value": fl / dt / 1e12, "unit": "TFLOP/s",
-                "sample": f"{rows_n} sampled output rows, keys/values for all {V} rows"}
+        return {"seconds": round(dt, 3), "value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s",
+                "sample": f"{rows_n} sampled output rows, keys/values for all {V} rows",
+                "full_block_s_est": round(block_flops(V, D, F) / (fl / dt), 2)}
 
-    # ---- single blocks: the 640-token block, the H3-scale block, one block of each loop ----
-    for name, rows_n in (("block_small", None), ("loop_4blk", None), ("block_h3", 256),
-                         ("loop_8blk_32k", 256)):
+    def single_block(name, rows_n):
         wl = I.WORKLOADS[name]
         log(f"[configs] block {name}")
         case = I.block_case(wl, seed=0, n_blocks=1)
@@ -217,157 +229,201 @@ def configs_report(args):
         ms = gpu_ms(lambda: N.dit_block_forward(dims, lay, blk.weights, temb, x, out,
                                                 N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
         fl = block_flops(wl.n_valid, wl.hidden, wl.ffn)
-        orc = oracle_block(case, rows_n)
         emit({"workload": name, "kind": "block", "valid": wl.n_valid, "seq_pad": wl.seq_pad,
               "hidden": wl.hidden, "ffn": wl.ffn, "heads": wl.heads, "head_dim": wl.head_dim,
               "useful_flops": fl, "gpu_ms": round(ms, 4), "gpu_tflops": round(fl / ms / 1e9, 2),
               "frac_of_2.5PF": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-              "oracle": {**orc, "value": round(orc["value"], 5)},
-              "oracle_full_block_s_est": round(fl / (orc["value"] * 1e12), 2)})
-        del ws, blk, x, out
+              "oracle": oracle_block(case, rows_n)})
 
-    # ---- the 4-block 49-interval loop, cache off and conservative ----
-    wl = I.WORKLOADS["loop_4blk"]
-    log("[configs] loop loop_4blk")
-    case = I.loop_case(wl, seed=0)
-    dims, lay = dev.dims_of(wl), dev.layout_of(wl)
-    blocks = dev.upload_blocks(case.blocks)
-    bw = [b.weights for b in blocks]
-    temb = dev.to_dev_f32(case.temb_steps)
-    x0 = dev.to_dev_f32(case.x0)
-    x = torch.empty_like(x0)
-    ws, _ = dev.workspace(dims, lay, len(blocks))
-    res = {}
-    for mode in ("off", "conservative"):
-        pol = N.make_policy(mode)
-        stats = {}
+    def loop_4blk():
+        wl = I.WORKLOADS["loop_4blk"]
+        log("[configs] loop loop_4blk")
+        case = I.loop_case(wl, seed=0)
+        dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+        blocks = dev.upload_blocks(case.blocks)
+        bw = [b.weights for b in blocks]
+        temb = dev.to_dev_f32(case.temb_steps)
+        x0 = dev.to_dev_f32(case.x0)
+        x = torch.empty_like(x0)
+        ws, _ = dev.workspace(dims, lay, len(blocks))
+        res, finals = {}, {}
+        for mode in ("off", "conservative"):
+            pol = N.make_policy(mode)
+            stats = {}
 
-        def run():
-            x.copy_(x0)
-            stats["s"] = N.denoise_loop(dims, lay, bw, wl.n_intervals, case.sigmas_video,
-                                        case.sigmas_audio, temb, pol, x, N.DIT_ATTN_VALID_ONLY,
-                                        ws, stream=stream, want_hits=False)[0]
-        ms = gpu_ms(run, warm=1, reps=3)
-        st = stats["s"]
-        res[mode] = {"ms_per_loop": round(ms, 3), "steps_per_sec": round(wl.n_intervals / ms * 1e3, 2),
-                     "useful_tflops": round(st.useful_flops / ms / 1e9, 2),
-                     "dit_calls": st.dit_calls, "cache_hits": st.cache_hits}
-    one = I.block_case(wl, seed=0, n_blocks=1)
-    orc = oracle_block(one, None)
-    t_blk = orc["seconds"]
-    ext = {m: round(r["dit_calls"] * wl.n_blocks * t_blk, 1) for m, r in res.items()}
-    emit({"workload": wl.name, "kind": "loop", "intervals": wl.n_intervals, "blocks": wl.n_blocks,
-          "valid": wl.n_valid, "gpu": res,
-          "oracle": {"one_block_seconds": t_blk, "loop_seconds_extrapolated": ext,
-                     "note": "extrapolated: dit_calls x blocks x one float64 block (Euler steps negligible)"}})
-    del ws, blocks, x, x0
+            def run():
+                x.copy_(x0)
+                stats["s"] = N.denoise_loop(dims, lay, bw, wl.n_intervals, case.sigmas_video,
+                                            case.sigmas_audio, temb, pol, x, N.DIT_ATTN_VALID_ONLY,
+                                            ws, stream=stream, want_hits=False)[0]
+            ms = gpu_ms(run, warm=1, reps=3)
+            st = stats["s"]
+            finals[mode] = x[: wl.n_valid].cpu().numpy()
+            res[mode] = {"ms_per_loop": round(ms, 3),
+                         "steps_per_sec": round(wl.n_intervals / ms * 1e3, 2),
+                         "useful_tflops": round(st.useful_flops / ms / 1e9, 2),
+                         "frac_of_2.5PF": round(st.useful_flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                         "dit_calls": st.dit_calls, "cache_hits": st.cache_hits}
+        rec = {"workload": wl.name, "kind": "loop", "intervals": wl.n_intervals,
+               "blocks": wl.n_blocks, "valid": wl.n_valid, "gpu": res,
+               "quality_conservative_vs_off": latent_compare(finals["conservative"], finals["off"])}
+        if run_oracle:
+            orc = oracle_block(I.block_case(wl, seed=0, n_blocks=1), None)
+            t_blk = orc["seconds"]
+            rec["oracle"] = {"one_block_seconds": t_blk,
+                             "loop_seconds_extrapolated": {
+                                 m: round(r["dit_calls"] * wl.n_blocks * t_blk, 1)
+                                 for m, r in res.items()},
+                             "note": "extrapolated: dit_calls x blocks x one float64 block "
+                                     "(Euler steps negligible)"}
+        emit(rec)
 
-    # ---- a batch of 4 ragged requests through one H3-scale block: batched vs one call each ----
-    log("[configs] batched block")
-    cfg = I.BLOCK_RAGGED
-    L, reqs = cfg["seq_pad"], cfg["requests"]
-    B = len(reqs)
-    wl = I.Workload("block_ragged", cfg["hidden"], cfg["heads"], cfg["head_dim"], cfg["ffn"],
-                    reqs[0][0], reqs[0][1], L)
-    rng = np.random.Generator(np.random.PCG64(3))
-    blk_p = I.make_block(rng, wl)
-    D = wl.hidden
-    xb = np.zeros((B * L, D), np.uint16)
-    for b, (nv, na) in enumerate(reqs):
-        xb[b * L: b * L + nv + na] = I.bf16_bits(rng.standard_normal((nv + na, D), dtype=np.float32))
-    temb_b = rng.standard_normal((B, 2, 6, D), dtype=np.float32)
-    dims, blk = dev.dims_of(wl), dev.upload_block(blk_p)
-    lays = [N.make_layout(nv, na, L) for nv, na in reqs]
-    x, temb = dev.to_dev_bf16(xb), dev.to_dev_f32(temb_b)
-    out = torch.empty_like(x)
-    nbytes, _ = N.dit_workspace_size_batched(dims, lays)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    ms_b = gpu_ms(lambda: N.dit_block_forward_batched(dims, lays, blk.weights, temb, x, out,
-                                                      N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
+    def block_ragged():
+        log("[configs] batched block")
+        cfg = I.BLOCK_RAGGED
+        L, reqs = cfg["seq_pad"], cfg["requests"]
+        B = len(reqs)
+        wl = I.Workload("block_ragged", cfg["hidden"], cfg["heads"], cfg["head_dim"], cfg["ffn"],
+                        reqs[0][0], reqs[0][1], L)
+        rng = np.random.Generator(np.random.PCG64(3))
+        blk_p = I.make_block(rng, wl)
+        D = wl.hidden
+        xb = np.zeros((B * L, D), np.uint16)
+        for b, (nv, na) in enumerate(reqs):
+            xb[b * L: b * L + nv + na] = I.bf16_bits(rng.standard_normal((nv + na, D),
+                                                                         dtype=np.float32))
+        temb_b = rng.standard_normal((B, 2, 6, D), dtype=np.float32)
+        dims, blk = dev.dims_of(wl), dev.upload_block(blk_p)
+        lays = [N.make_layout(nv, na, L) for nv, na in reqs]
+        x, temb = dev.to_dev_bf16(xb), dev.to_dev_f32(temb_b)
+        out = torch.empty_like(x)
+        nbytes, _ = N.dit_workspace_size_batched(dims, lays)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ms_b = gpu_ms(lambda: N.dit_block_forward_batched(dims, lays, blk.weights, temb, x, out,
+                                                          N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
 
-    def singles():
-        for b in range(B):
-            N.dit_block_forward(dims, lays[b], blk.weights, temb[b], x[b * L:(b + 1) * L],
-                                out[b * L:(b + 1) * L], N.DIT_ATTN_VALID_ONLY, ws, stream=stream)
-    ms_s = gpu_ms(singles)
-    fl = sum(block_flops(nv + na, D, wl.ffn) for nv, na in reqs)
-    one = I.BlockCase(wl, [blk_p], xb[:L], temb_b[0])      # wl holds request 0's layout
-    orc = oracle_block(one, 64)
-    emit({"workload": "block_ragged", "kind": "batched block", "batch": B, "seq_pad": L,
-          "hidden": D, "ffn": wl.ffn, "heads": wl.heads, "head_dim": wl.head_dim,
-          "valid": [nv + na for nv, na in reqs], "useful_flops": fl,
-          "gpu": {"batched": {"ms": round(ms_b, 4), "useful_tflops": round(fl / ms_b / 1e9, 2)},
-                  "one_call_per_request": {"ms": round(ms_s, 4),
-                                           "useful_tflops": round(fl / ms_s / 1e9, 2)}},
-          "oracle": {**orc, "value": round(orc["value"], 5),
-                     "sample": "request 0: " + orc["sample"]}})
-    del ws, blk, x, out
+        def singles():
+            for b in range(B):
+                N.dit_block_forward(dims, lays[b], blk.weights, temb[b], x[b * L:(b + 1) * L],
+                                    out[b * L:(b + 1) * L], N.DIT_ATTN_VALID_ONLY, ws,
+                                    stream=stream)
+        ms_s = gpu_ms(singles)
+        fl = sum(block_flops(nv + na, D, wl.ffn) for nv, na in reqs)
+        orc = oracle_block(I.BlockCase(wl, [blk_p], xb[:L], temb_b[0]), 64)
+        if orc:
+            orc["sample"] = "request 0: " + orc["sample"]
+        emit({"workload": "block_ragged", "kind": "batched block", "batch": B, "seq_pad": L,
+              "hidden": D, "ffn": wl.ffn, "heads": wl.heads, "head_dim": wl.head_dim,
+              "valid": [nv + na for nv, na in reqs], "useful_flops": fl,
+              "gpu": {"batched": {"ms": round(ms_b, 4), "useful_tflops": round(fl / ms_b / 1e9, 2)},
+                      "one_call_per_request": {"ms": round(ms_s, 4),
+                                               "useful_tflops": round(fl / ms_s / 1e9, 2)}},
+              "oracle": orc})
 
-    # ---- the velocity head on the 32768-token H3-scale stack output ----
-    log("[configs] velocity head")
-    wl = I.WORKLOADS["loop_8blk_32k"]
-    rng = np.random.Generator(np.random.PCG64(4))
-    hp = I.make_head(rng, wl)
-    C = hp.w_out.shape[1]
-    xh = dev.to_dev_bf16(I.make_activation_bf16(rng, wl))
-    th = dev.to_dev_f32(rng.standard_normal((2, 2, wl.hidden), dtype=np.float32))
-    hw = [dev.to_dev_f32(hp.norm_g), dev.to_dev_f32(hp.ada), dev.to_dev_bf16(hp.w_out),
-          dev.to_dev_f32(hp.bias)]
-    head = N.make_head(*hw, C)
-    dims, lay = dev.dims_of(wl), dev.layout_of(wl)
-    ws = torch.empty(N.dit_head_workspace_size(dims, lay, C), dtype=torch.uint8, device="cuda")
-    vh = torch.empty((wl.seq_pad, C), dtype=torch.float32, device="cuda")
-    ms = gpu_ms(lambda: N.dit_velocity_head(dims, lay, head, th, xh, vh, ws, stream=stream))
-    V, D, L = wl.n_valid, wl.hidden, wl.seq_pad
-    min_bytes = 2.0 * V * D + 4.0 * L * C + 2.0 * 2 * C * D      # x in, v out, weights
-    run_bytes = min_bytes + 4.0 * V * D                           # + the bf16 h round trip
-    fl = 2.0 * V * D * C
-    t0 = time.perf_counter()
-    rows = np.sort(np.random.default_rng(5).choice(V, 1024, replace=False))
-    xo = I.bf16_to_f32(dev.bf16_bits_of(xh)[rows]).astype(np.float64)
-    hf = hp.as_float()
-    O.velocity_head(xo, hf["norm_g"], hf["ada"], th.cpu().numpy(), hf["w_out"], hf["bias"],
-                    O.Layout(len(rows), 0, len(rows)), 1e-6)
-    dt = time.perf_counter() - t0
-    emit({"workload": "head_32k", "kind": "velocity head", "valid": V, "seq_pad": L, "hidden": D,
-          "channels": C, "gpu_ms": round(ms, 4),
-          "min_hbm_bytes": min_bytes, "kernel_hbm_bytes": run_bytes,
-          "gbps_min": round(min_bytes / ms / 1e6, 1), "gbps_kernels": round(run_bytes / ms / 1e6, 1),
-          "frac_of_8TBs_kernels": round(run_bytes / ms / 1e6 / 8000.0, 4),
-          "useful_tflops": round(fl / ms / 1e9, 2),
-          "oracle": {"seconds": round(dt, 3), "value": round(2.0 * len(rows) * D * C / dt / 1e12, 5),
-                     "unit": "TFLOP/s", "sample": f"{len(rows)} rows (video), whole head"}})
-    del ws, xh, vh, hw
+    def head_32k():
+        log("[configs] velocity head")
+        wl = I.WORKLOADS["loop_8blk_32k"]
+        rng = np.random.Generator(np.random.PCG64(4))
+        hp = I.make_head(rng, wl)
+        C = hp.w_out.shape[1]
+        xh = dev.to_dev_bf16(I.make_activation_bf16(rng, wl))
+        th = dev.to_dev_f32(rng.standard_normal((2, 2, wl.hidden), dtype=np.float32))
+        hw = [dev.to_dev_f32(hp.norm_g), dev.to_dev_f32(hp.ada), dev.to_dev_bf16(hp.w_out),
+              dev.to_dev_f32(hp.bias)]
+        head = N.make_head(*hw, C)
+        dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+        ws = torch.empty(N.dit_head_workspace_size(dims, lay, C), dtype=torch.uint8, device="cuda")
+        vh = torch.empty((wl.seq_pad, C), dtype=torch.float32, device="cuda")
+        ms = gpu_ms(lambda: N.dit_velocity_head(dims, lay, head, th, xh, vh, ws, stream=stream))
+        V, D, L = wl.n_valid, wl.hidden, wl.seq_pad
+        min_bytes = 2.0 * V * D + 4.0 * L * C + 2.0 * 2 * C * D      # x in, v out, weights
+        run_bytes = min_bytes + 4.0 * V * D                           # + the bf16 h round trip
+        fl = 2.0 * V * D * C
+        rec = {"workload": "head_32k", "kind": "velocity head", "valid": V, "seq_pad": L,
+               "hidden": D, "channels": C, "gpu_ms": round(ms, 4),
+               "min_hbm_bytes": min_bytes, "kernel_hbm_bytes": run_bytes,
+               "gbps_min": round(min_bytes / ms / 1e6, 1),
+               "gbps_kernels": round(run_bytes / ms / 1e6, 1),
+               "frac_of_8TBs_kernels": round(run_bytes / ms / 1e6 / 8000.0, 4),
+               "useful_tflops": round(fl / ms / 1e9, 2)}
+        if run_oracle:
+            t0 = time.perf_counter()
+            rows = np.sort(np.random.default_rng(5).choice(V, 1024, replace=False))
+            xo = I.bf16_to_f32(dev.bf16_bits_of(xh)[rows]).astype(np.float64)
+            hf = hp.as_float()
+            O.velocity_head(xo, hf["norm_g"], hf["ada"], th.cpu().numpy(), hf["w_out"], hf["bias"],
+                            O.Layout(len(rows), 0, len(rows)), 1e-6)
+            dt = time.perf_counter() - t0
+            rec["oracle"] = {"seconds": round(dt, 3),
+                             "value": round(2.0 * len(rows) * D * C / dt / 1e12, 5),
+                             "unit": "TFLOP/s", "sample": f"{len(rows)} rows (video), whole head"}
+        emit(rec)
 
-    # ---- ragged valid-only attention: 4 requests of 8192 rows, 16 heads x 128 ----
-    log("[configs] attention ragged")
-    B, L, H, Dh = 4, 8192, 16, 128
-    valid = (3000, 5100, 7777, 8192)
-    q, k, v = I.attention_case(B, L, H, Dh, valid, seed=7)
-    dq, dk, dv = (dev.to_dev_bf16(t) for t in (q, k, v))
-    do = torch.empty((B, L, H, Dh), dtype=torch.bfloat16, device="cuda")
-    useful = sum(4.0 * n * n * H * Dh for n in valid)
-    launched = 4.0 * B * L * L * H * Dh
-    out = {}
-    for mode, name in ((N.DIT_ATTN_VALID_ONLY, "valid_only"), (N.DIT_ATTN_FIXED_VALID, "fixed_valid")):
-        ms = gpu_ms(lambda: N.dit_attention_forward(dq, dk, dv, do, B, L, H, Dh, L * H * Dh, H * Dh,
-                                                    L * H * Dh, H * Dh, valid, mode, stream=stream))
-        out[name] = {"ms": round(ms, 4), "useful_tflops": round(useful / ms / 1e9, 2)}
-    rows_per = 64
-    dt = 0.0
-    for b, n in enumerate(valid):
-        rows = np.sort(np.random.default_rng(b).choice(n, rows_per, replace=False))
-        qb, kb, vb = (I.bf16_to_f32(t[b, :n]).astype(np.float64) for t in (q, k, v))
-        t0 = time.perf_counter()
-        O.attention_rows(qb[rows], kb, vb, n)
-        dt += time.perf_counter() - t0
-    fl = sum(4.0 * rows_per * n * H * Dh for n in valid)
-    emit({"workload": "attn_ragged", "kind": "attention", "batch": B, "seq_pad": L, "heads": H,
-          "head_dim": Dh, "valid": list(valid), "useful_flops": useful,
-          "fixed_valid_launched_flops": launched, "useful_over_launched": round(useful / launched, 4),
-          "gpu": out, "oracle": {"seconds": round(dt, 3), "value": round(fl / dt / 1e12, 5),
-                                 "unit": "TFLOP/s",
-                                 "sample": f"{rows_per} query rows per request, all heads and keys"}})
+    def attn_ragged(qk_normed):
+        """4 requests of 8192 rows, 16 heads x 128, valid {3000, 5100, 7777, 8192}: q, k, v
+        N(0, 1) as drawn (the kernel then keeps the exact running maximum), or, qk_normed, q and k
+        passed through the per-head Q/K RMSNorm (unit gains, handed to the kernel) as inside the
+        block, which bounds the logits."""
+        name = "attn_ragged_qknorm" if qk_normed else "attn_ragged"
+        log(f"[configs] {name}")
+        B, L, H, Dh = 4, 8192, 16, 128
+        valid = (3000, 5100, 7777, 8192)
+        q, k, v = I.attention_case(B, L, H, Dh, valid, seed=7)
+        gains = None
+        if qk_normed:
+            g = np.ones(Dh, np.float32)
+            for t in (q, k):
+                f = I.bf16_to_f32(t).astype(np.float64)
+                ms_ = np.mean(f * f, axis=-1, keepdims=True)
+                t[...] = I.bf16_bits(np.where(ms_ > 0, f / np.sqrt(ms_ + 1e-6), 0.0))
+            gains = (dev.to_dev_f32(g), dev.to_dev_f32(g))
+        dq, dk, dv = (dev.to_dev_bf16(t) for t in (q, k, v))
+        do = torch.empty((B, L, H, Dh), dtype=torch.bfloat16, device="cuda")
+        useful = sum(4.0 * n * n * H * Dh for n in valid)
+        launched = 4.0 * B * L * L * H * Dh
+        out = {}
+        for mode, mname in ((N.DIT_ATTN_VALID_ONLY, "valid_only"),
+                            (N.DIT_ATTN_FIXED_VALID, "fixed_valid")):
+            kw = {} if gains is None else {"q_gain": gains[0], "k_gain": gains[1]}
+            ms = gpu_ms(lambda: N.dit_attention_forward(dq, dk, dv, do, B, L, H, Dh, L * H * Dh,
+                                                        H * Dh, L * H * Dh, H * Dh, valid, mode,
+                                                        stream=stream, **kw))
+            out[mname] = {"ms": round(ms, 4), "useful_tflops": round(useful / ms / 1e9, 2),
+                          "frac_of_2.5PF": round(useful / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        rec = {"workload": name, "kind": "attention", "batch": B, "seq_pad": L, "heads": H,
+               "head_dim": Dh, "valid": list(valid), "useful_flops": useful,
+               "qk_normed_with_gains": qk_normed,
+               "fixed_valid_launched_flops": launched,
+               "useful_over_launched": round(useful / launched, 4), "gpu": out}
+        if run_oracle:
+            rows_per = 64
+            dt = 0.0
+            for b, n in enumerate(valid):
+                rows = np.sort(np.random.default_rng(b).choice(n, rows_per, replace=False))
+                qb, kb, vb = (I.bf16_to_f32(t[b, :n]).astype(np.float64) for t in (q, k, v))
+                t0 = time.perf_counter()
+                O.attention_rows(qb[rows], kb, vb, n)
+                dt += time.perf_counter() - t0
+            fl = sum(4.0 * rows_per * n * H * Dh for n in valid)
+            rec["oracle"] = {"seconds": round(dt, 3), "value": round(fl / dt / 1e12, 5),
+                             "unit": "TFLOP/s",
+                             "sample": f"{rows_per} query rows per request, all heads and keys"}
+        emit(rec)
+
+    for name, rows_n in (("block_small", None), ("loop_4blk", None), ("block_h3", 256),
+                         ("loop_8blk_32k", 256)):
+        if want(name):
+            single_block(name, rows_n)
+    if want("loop_4blk_loop"):
+        loop_4blk()
+    if want("block_ragged"):
+        block_ragged()
+    if want("head_32k"):
+        head_32k()
+    if want("attn_ragged"):
+        attn_ragged(False)
+    if want("attn_ragged_qknorm"):
+        attn_ragged(True)
 
 
 def main():
@@ -472,6 +528,11 @@ def main():
     achieved = attn_flops / t_attn / 1e12
     log(f"[bench] attention kernel: {t_attn * 1e3:.3f} ms, {achieved:.1f} TFLOP/s")
     if args.roofline_only:
+        # two Euler steps on the latent (velocity = the block output, bf16 copy of the latent),
+        # so that counter runs of this command also cover the step kernel
+        xs = x0.clone()
+        for _ in range(2):
+            N.step_update(xs, xout, xin, lay, D, -0.02, -0.02, stream=stream)
         # plain device copy of 1 GiB: calibrates FETCH_SIZE / WRITE_SIZE for the traffic figure
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
