@@ -514,6 +514,19 @@ static hipError_t gemm_dispatch_epi(const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// Compute units of the current device (queried once; 256 on MI355X).
+static long compute_units() {
+  static const long n = [] {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0)
+      return 256L;
+    return (long)cu;
+  }();
+  return n;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.N <= 0 || a.K <= 0) return hipErrorInvalidValue;
   // Epilogue vectors are 4 features wide and 8-byte aligned.
@@ -550,8 +563,18 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     valid_rows = 0;
     for (int b = 0; b < a.rows.batch; ++b) valid_rows += (a.rows.req_valid[b] + 255) / 256 * 256;
   }
+  // Choose the tile shape by the estimated time of its launch: rounds of tiles over the CUs
+  // times the time of one tile. A 256 x 256 direct-to-LDS tile (one per CU) does 4x the work of
+  // a 128 x 128 register-staged tile (two per CU) and takes about 1.2x as long per round
+  // (measured on the hidden-1024 projections: 28.6 us against 23.8 us per round at K = 1024),
+  // so few large tiles can still win over twice as many rounds of small ones.
+  const long cus = compute_units();
   const long tiles_big = (long)((valid_rows + 255) / 256) * ((a.N + out_big - 1) / out_big);
-  const bool big = tiles_big >= 512;
+  const int out_small = (a.epilogue == EPI_SWIGLU) ? 64 : 128;
+  const long tiles_small = (long)((valid_rows + 127) / 128) * ((a.N + out_small - 1) / out_small);
+  const double t_big = 1.2 * (double)((tiles_big + cus - 1) / cus);
+  const double t_small = (double)((tiles_small + 2 * cus - 1) / (2 * cus));
+  const bool big = t_big < t_small;
   if (aligned && big && (a.K % kDlBK) == 0) {
     const int tiles_m = (total_rows(a.rows) + 255) / 256;
     const int tiles_n = (a.N + out_big - 1) / out_big;
