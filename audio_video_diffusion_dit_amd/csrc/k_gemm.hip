@@ -101,6 +101,37 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&
                          (EPI == EPI_GATED_F32_TO_F32);
   constexpr bool OUT_F32 =
       (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32) || (EPI == EPI_BIAS_TO_F32);
+  constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
+  // Gate values (ada + temb of the row's request and modality) of this lane's features. When all
+  // rows of the wave's token range belong to one request and one modality (every tile but the
+  // one holding a video/audio or request boundary), they are loaded once for the whole range
+  // instead of once per row: wave-uniform test on the range's first and last row.
+  float gv[OUT_T][4][4];
+  bool gate_once = false;
+  auto load_gate = [&](int mod, int req) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < OUT_T; ++f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int fb0 = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
+        const int fb = fb0 < a.N ? fb0 : a.N - 4;
+        const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
+        const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
+        const float4 gt = *reinterpret_cast<const float4*>(a.temb + req * a.temb_stride + goff);
+        gv[f][j][0] = ga.x + gt.x; gv[f][j][1] = ga.y + gt.y;
+        gv[f][j][2] = ga.z + gt.z; gv[f][j][3] = ga.w + gt.w;
+      }
+    }
+  };
+  if constexpr (GATED) {
+    const int tok0 = m0 + wm * TM;
+    if (tok0 < rows_total) {
+      const int tok1 = (tok0 + TM <= rows_total ? tok0 + TM : rows_total) - 1;
+      const RowInfo r0 = row_info(a.rows, tok0), r1 = row_info(a.rows, tok1);
+      gate_once = r0.req == r1.req && r0.mod == r1.mod;
+      if (gate_once) load_gate(r0.mod, r0.req);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int tok = m0 + wm * TM + t * 32 + l32;
@@ -108,15 +139,14 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&
     const RowInfo ri = row_info(a.rows, tok);
     const bool valid = ri.valid;
     const int mod = ri.mod;
-    constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
     // Gated epilogues: every load of this token row (residual and gate values) is issued before
     // the row's first store, so they share one memory round trip. The compiler cannot prove that
     // the output stores do not alias them and would otherwise keep each load group behind the
     // previous store. Feature offsets past N are clamped to a valid address (the values are
     // then discarded).
     float rv[OUT_T][4][4];
-    float gv[OUT_T][4][4];
     if constexpr (GATED) {
+      if (!gate_once) load_gate(mod, ri.req);
 #pragma unroll
       for (int f = 0; f < OUT_T; ++f) {
 #pragma unroll
@@ -133,11 +163,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&
                 static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
             rv[f][j][0] = rr.x; rv[f][j][1] = rr.y; rv[f][j][2] = rr.z; rv[f][j][3] = rr.w;
           }
-          const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
-          const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
-          const float4 gt = *reinterpret_cast<const float4*>(a.temb + ri.req * a.temb_stride + goff);
-          gv[f][j][0] = ga.x + gt.x; gv[f][j][1] = ga.y + gt.y;
-          gv[f][j][2] = ga.z + gt.z; gv[f][j][3] = ga.w + gt.w;
         }
       }
     }
