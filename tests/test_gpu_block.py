@@ -232,3 +232,47 @@ def test_block_32k_sampled_rows(env):
                                    edges]))
     check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl,
                 "32k block sampled rows", rows=rows)
+
+
+@pytest.mark.parametrize("nv,na,L", [(0, 0, 256), (0, 300, 320), (250, 0, 256)])
+def test_block_degenerate_layouts(env, nv, na, L):
+    """No valid row (the output is all zero), audio rows only, video rows only: against the
+    oracle and its storage diagnostic; fixed-valid equals valid-only bit for bit."""
+    N, dev = env
+    from audio_video_diffusion_dit_amd import inputs as I
+    wl = I.Workload("block_degenerate", 256, 2, 128, 300, nv, na, L)
+    case = I.block_case(wl, seed=nv + 3 * na + L, n_blocks=1)
+    say(f"block degenerate layout: video {nv} audio {na} seq_pad {L}")
+    out, _, _ = _gpu_block(env, case)
+    fv, _, _ = _gpu_block(env, case, attn_mode=N.DIT_ATTN_FIXED_VALID)
+    assert np.array_equal(dev.bf16_bits_of(out), dev.bf16_bits_of(fv))
+    got = dev.bf16_values_of(out).astype(np.float64)
+    V = wl.n_valid
+    assert np.all(got[V:] == 0)
+    if V == 0:
+        return
+    check_block(got, x_values(case.x), case.blocks[0], case.temb, wl,
+                f"block, video {nv} audio {na}")
+
+
+def test_block_largest_sequence_at_hidden_3072(env):
+    """The longest sequence the library takes at hidden 3072: 116,508 rows, whose q/k/v rows
+    [seq_pad, 3D] span 2,147,475,456 bytes, just under the 2 GiB the kernels' 32-bit buffer
+    offsets address (one row more is rejected during validation). Sampled rows, including the
+    last ones, against the oracle with keys and values for every row."""
+    N, dev = env
+    from audio_video_diffusion_dit_amd import inputs as I
+    wl = I.Workload("block_max", 3072, 24, 128, 8192, 110000, 6508, 116508)
+    assert wl.seq_pad * 3 * wl.hidden * 2 < 2 ** 31 <= (wl.seq_pad + 1) * 3 * wl.hidden * 2
+    case = I.block_case(wl, seed=8, n_blocks=1)
+    V = wl.n_valid
+    say(f"block at the largest sequence: V={V} L={wl.seq_pad}")
+    out, _, _ = _gpu_block(env, case)
+    got = dev.bf16_values_of(out).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(116)
+    edges = [0, 65535, 65536, wl.n_video - 1, wl.n_video, V - 2, V - 1]
+    rows = np.sort(np.concatenate([rng.choice(np.setdiff1d(np.arange(V), edges), 25, replace=False),
+                                   edges]))
+    check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl,
+                "largest-sequence block sampled rows", rows=rows)
