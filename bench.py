@@ -56,6 +56,10 @@ def parse():
     p.add_argument("--configs", action="store_true",
                    help="per-workload report instead of the bench line: GPU and float64-oracle "
                         "timings of every configuration, one JSON line each")
+    p.add_argument("--hbm-reference", action="store_true",
+                   help="time the vendor device copy (and an fp32->bf16 conversion) of the same "
+                        "byte counts as each HBM-bound kernel of the 32k block, next to five block "
+                        "calls, for a kernel trace of both")
     p.add_argument("--only", default=None,
                    help="with --configs: comma-separated subset of block_small, loop_4blk, "
                         "block_h3, loop_8blk_32k, loop_4blk_loop, block_ragged, head_32k, "
@@ -426,6 +430,72 @@ def configs_report(args):
         attn_ragged(True)
 
 
+def hbm_reference(args):
+    """Same-size reference for the HBM-bound kernels: the library's own device copy (or, where
+    reads and writes differ, an fp32->bf16 conversion) moving exactly the bytes each kernel of the
+    32k block must move. Run under rocprofv3 --kernel-trace to set both side by side."""
+    import statistics
+    import torch
+    from audio_video_diffusion_dit_amd import _native as N
+    from audio_video_diffusion_dit_amd import device as dev
+    from audio_video_diffusion_dit_amd import inputs as I
+
+    torch.cuda.set_device(0)
+    wl = I.WORKLOADS["loop_8blk_32k"]
+    case = I.block_case(wl, seed=0, n_blocks=1)
+    dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+    blk = dev.upload_block(case.blocks[0])
+    x = dev.to_dev_bf16(case.x)
+    temb = dev.to_dev_f32(case.temb)
+    out = torch.empty_like(x)
+    ws, _ = dev.workspace(dims, lay, 0)
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        N.dit_block_forward(dims, lay, blk.weights, temb, x, out, 0, ws, stream=stream)
+    torch.cuda.synchronize()
+    del ws, blk, x, out, temb
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=20, rounds=3):
+        # reps back-to-back calls between two events: the launch latency of a lone call (tens of
+        # microseconds) is not counted
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(rounds):
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        return statistics.median(ts)
+
+    VD = wl.seq_pad * wl.hidden
+    cases = [("norm1 + AdaLN: read x bf16, write h bf16", 2 * VD, 2 * VD),
+             ("norm2 + AdaLN: read x1 fp32, write h2 bf16", 4 * VD, 2 * VD),
+             ("Q/K norm + RoPE: read and write q, k bf16", 4 * VD, 4 * VD),
+             ("Euler step: read x fp32 + v bf16, write x fp32 + bf16 copy", 6 * VD, 6 * VD)]
+    print("| bytes of | reference | time | rate | % of 8 TB/s |")
+    print("|---|---|---|---|---|")
+    for label, rb, wb in cases:
+        if rb == wb:
+            a = torch.empty(rb // 2, dtype=torch.bfloat16, device="cuda").normal_()
+            b = torch.empty_like(a)
+            ms = timed(lambda: b.copy_(a))
+            kind = "device copy"
+        else:
+            a = torch.empty(rb // 4, dtype=torch.float32, device="cuda").normal_()
+            b = torch.empty(wb // 2, dtype=torch.bfloat16, device="cuda")
+            ms = timed(lambda: b.copy_(a))
+            kind = "fp32 -> bf16 conversion"
+        tb = (rb + wb) / ms / 1e9
+        print(f"| {label} | {kind} | {ms * 1e3:.1f} us | {tb:.2f} TB/s | {tb / 8 * 100:.0f}% |", flush=True)
+        del a, b
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -435,6 +505,9 @@ def main():
 
     if args.configs:
         configs_report(args)
+        return
+    if args.hbm_reference:
+        hbm_reference(args)
         return
 
     import numpy as np
