@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libavdit.so")
 
-SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "abi.cpp", "noalloc.hip"]
+SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "k_head.hip", "abi.cpp", "noalloc.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -47,7 +47,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

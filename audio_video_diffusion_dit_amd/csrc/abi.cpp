@@ -712,31 +712,9 @@ constexpr int32_t kMaxOutChannels = 1 << 16;
 // A projection to few channels carries little matrix work per k-tile, so one workgroup's walk
 // over the reduction is a chain of load latencies: for C <= 256 the reduction is split four
 // ways (fp32 partials in the workspace, summed in order by one reduction pass).
-constexpr int kHeadSplits = 4;
-
-int head_splits(const dit_dims* d, int32_t C) {
-  return (C <= 256 && d->hidden % (kHeadSplits * 64) == 0) ? kHeadSplits : 1;
-}
-
-// workspace: h [seq_pad, D] bf16, then (split reduction) the partials [splits, seq_pad, C] fp32
-size_t head_h_bytes(const dit_dims* d, const dit_layout* l) {
-  return align_up((size_t)l->seq_pad * d->hidden * 2);
-}
-
-size_t head_ws_bytes(const dit_dims* d, const dit_layout* l, int32_t C) {
-  size_t n = head_h_bytes(d, l);
-  const int S = head_splits(d, C);
-  if (S > 1) n += align_up((size_t)S * l->seq_pad * C * 4);
-  return n < kAlign ? kAlign : n;
-}
-
-// The projection reads h [seq_pad, D] and one modality's weight [C, D] through 32-bit buffer
-// offsets.
-int check_head_spans(const dit_dims* d, const dit_layout* l, int32_t C) {
-  int st;
-  if ((st = check_span((int64_t)l->seq_pad * d->hidden * 2, "the head input rows [seq_pad, D]")) != DIT_OK)
-    return st;
-  return check_span((int64_t)C * d->hidden * 2, "one modality's output weight [C, D]");
+// workspace: the folded table, mul [2, D] then cst [2, C] (fp32)
+size_t head_ws_bytes(const dit_dims* d, int32_t C) {
+  return align_up((size_t)2 * d->hidden * 4) + align_up((size_t)2 * C * 4);
 }
 
 int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_weights* hw,
@@ -761,8 +739,7 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
   if ((st = check_aligned16(temb, "temb")) != DIT_OK) return st;
   if ((st = check_aligned16(hw->norm_g, "norm_g")) != DIT_OK) return st;
   if ((st = check_aligned16(hw->ada, "ada")) != DIT_OK) return st;
-  if ((st = check_head_spans(dims, layout, C)) != DIT_OK) return st;
-  const size_t need = head_ws_bytes(dims, layout, C);
+  const size_t need = head_ws_bytes(dims, C);
   if ((st = check_ws(ws, ws_bytes, need)) != DIT_OK) return st;
   const int32_t D = dims->hidden, L = layout->seq_pad;
   const int32_t nv = layout->n_video, V = layout->n_video + layout->n_audio;
@@ -773,39 +750,28 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
   if (L == 0) return DIT_OK;
   (void)hipGetLastError();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* h = static_cast<uint16_t*>(ws);
+  float* mul = static_cast<float*>(ws);
+  float* cst = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)2 * D * 4));
 
-  NormModArgs n{};
-  n.x = x; n.h = h; n.gain = hw->norm_g; n.ada = hw->ada; n.temb = temb;
-  n.rows = RowLayout{nv, V, L}; n.D = D; n.shift_chunk = 0; n.scale_chunk = 1;
-  n.eps = dims->norm_eps; n.x_f32 = f32 ? 1 : 0; n.temb_stride = 0; n.table_rows = 2;
-  if ((st = device_status(launch_norm_mod(n, s), "final norm+modulation")) != DIT_OK) return st;
+  HeadPrepArgs p{};
+  p.gain = hw->norm_g; p.ada = hw->ada; p.temb = temb; p.w = hw->w_out; p.bias = hw->bias;
+  p.mul = mul; p.cst = cst; p.D = D; p.C = C;
+  if ((st = device_status(launch_head_prep(p, s), "head table fold")) != DIT_OK) return st;
 
-  // One launch per modality over its own rows; the audio launch also writes the zero tail.
-  // Row modality inside a launch comes from its RowLayout, which selects the bias row. With a
-  // split reduction the launches write fp32 partials and one pass adds them and the bias.
-  const int S = head_splits(dims, C);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + head_h_bytes(dims, layout));
-  const int64_t split_stride = (int64_t)L * C;
+  // Both modalities in one launch, each over its own rows; the audio rows include the zero tail.
+  HeadProjArgs a{};
   for (int m = 0; m < 2; ++m) {
     const int32_t r0 = m == 0 ? 0 : nv;
-    const int32_t rows = m == 0 ? nv : L - nv;
-    if (rows <= 0) continue;
-    GemmArgs g{};
-    g.A = h + (size_t)r0 * D; g.W = hw->w_out + (size_t)m * C * D;
-    g.C = (S > 1 ? partials : v) + (size_t)r0 * C;
-    g.lda = D; g.ldw = D; g.ldc = C; g.N = C; g.K = D;
-    g.rows = m == 0 ? RowLayout{nv, nv, nv} : RowLayout{0, V - nv, L - nv};
-    g.epilogue = EPI_BIAS_TO_F32; g.bias = S > 1 ? nullptr : hw->bias;
-    g.k_splits = S; g.split_stride = split_stride;
-    if ((st = device_status(launch_gemm(g, s), "head projection")) != DIT_OK) return st;
+    a.x[m] = static_cast<const char*>(x) + (size_t)r0 * D * (f32 ? 4 : 2);
+    a.v[m] = v + (size_t)r0 * C;
+    a.w[m] = hw->w_out + (size_t)m * C * D;
+    a.mul[m] = mul + (size_t)m * D;
+    a.cst[m] = cst + (size_t)m * C;
+    a.rows[m] = m == 0 ? nv : L - nv;
+    a.valid[m] = m == 0 ? nv : V - nv;
   }
-  if (S > 1) {
-    SplitReduceArgs r{};
-    r.partials = partials; r.out = v; r.bias = hw->bias; r.rows = RowLayout{nv, V, L};
-    r.C = C; r.splits = S; r.split_stride = split_stride;
-    if ((st = device_status(launch_split_reduce(r, s), "head reduction")) != DIT_OK) return st;
-  }
+  a.D = D; a.C = C; a.ldv = C; a.eps = dims->norm_eps; a.x_f32 = f32 ? 1 : 0;
+  if ((st = device_status(launch_head_proj(a, s), "head projection")) != DIT_OK) return st;
   return DIT_OK;
 }
 
@@ -822,8 +788,7 @@ size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout,
          out_channels, kMaxOutChannels);
     return 0;
   }
-  if (check_head_spans(dims, layout, out_channels) != DIT_OK) return 0;
-  return head_ws_bytes(dims, layout, out_channels);
+  return head_ws_bytes(dims, out_channels);
 }
 
 int dit_velocity_head(const dit_dims* dims, const dit_layout* layout,

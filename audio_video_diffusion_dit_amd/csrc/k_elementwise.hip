@@ -380,43 +380,3 @@ hipError_t launch_step_update(const StepArgs& a, hipStream_t s) {
 }
 
 }  // namespace avdit
-
-// ---------------------------------------------------------------------------------------
-// Reduction of a split-K projection: one thread per 4 consecutive outputs of a row; the partial
-// sums are added in split order, so the result does not depend on scheduling.
-// ---------------------------------------------------------------------------------------
-namespace avdit {
-
-__global__ __launch_bounds__(256) void k_split_reduce(SplitReduceArgs a) {
-  const int c4 = a.C >> 2;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = (int64_t)total_rows(a.rows) * c4;
-  if (i >= n) return;
-  const int row = (int)(i / c4);
-  const int c = (int)(i - (int64_t)row * c4) * 4;
-  const RowInfo ri = row_info(a.rows, row);
-  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (ri.valid) {
-    const float* p = a.partials + (int64_t)row * a.C + c;
-    for (int s = 0; s < a.splits; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(p + s * a.split_stride);
-      o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
-    }
-    if (a.bias) {
-      const float4 b = *reinterpret_cast<const float4*>(a.bias + (int64_t)ri.mod * a.C + c);
-      o.x += b.x; o.y += b.y; o.z += b.z; o.w += b.w;
-    }
-  }
-  *reinterpret_cast<float4*>(a.out + (int64_t)row * a.C + c) = o;
-}
-
-hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s) {
-  if (a.C <= 0 || (a.C & 3) != 0 || a.splits < 1 || a.split_stride < (int64_t)total_rows(a.rows) * a.C)
-    return hipErrorInvalidValue;
-  const int64_t n = (int64_t)total_rows(a.rows) * (a.C / 4);
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-}  // namespace avdit

@@ -99,8 +99,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&
   const int rows_total = total_rows(a.rows);
   constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
                          (EPI == EPI_GATED_F32_TO_F32);
-  constexpr bool OUT_F32 =
-      (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32) || (EPI == EPI_BIAS_TO_F32);
+  constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
   constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
   // Gate values (ada + temb of the row's request and modality) of this lane's features. When all
   // rows of the wave's token range belong to one request and one modality (every tile but the
@@ -181,13 +180,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&
           } else if constexpr (GATED) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = fmaf(gv[f][j][i], acc[f][t][4 * j + i], rv[f][j][i]);
-          } else if constexpr (EPI == EPI_BIAS_TO_F32) {
-            float4 b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (a.bias) b = *reinterpret_cast<const float4*>(a.bias + (int64_t)mod * a.N + fb);
-            o[0] = acc[f][t][4 * j + 0] + b.x;
-            o[1] = acc[f][t][4 * j + 1] + b.y;
-            o[2] = acc[f][t][4 * j + 2] + b.z;
-            o[3] = acc[f][t][4 * j + 3] + b.w;
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
@@ -237,12 +229,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
 
   int tile_m, tile_n;
   select_tile(tiles_m, tiles_n, tile_m, tile_n);
-  // k split y = blockIdx.y (one split: y = 0, the whole reduction): operands advanced to the
-  // split's k range, fp32 partial output y
-  const int Kp = a.K / a.k_splits;
-  const uint16_t* const gA = a.A + (int64_t)blockIdx.y * Kp;
-  const uint16_t* const gW = a.W + (int64_t)blockIdx.y * Kp;
-  void* const gC = static_cast<float*>(a.C) + (int64_t)blockIdx.y * a.split_stride;
 
   const int m0 = tile_m * BM;
   const int rows_total = total_rows(a.rows);
@@ -260,8 +246,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
   if (rows_have_valid(a.rows, m0)) {
     const int ck = tid & 7;
     const int w_rows = (EPI == EPI_SWIGLU) ? a.up_offset + a.N : a.N;
-    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(gW, (uint32_t)((int64_t)w_rows * a.ldw * 2));
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(gA, (uint32_t)((int64_t)rows_total * a.lda * 2));
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(a.W, (uint32_t)((int64_t)w_rows * a.ldw * 2));
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a.A, (uint32_t)((int64_t)rows_total * a.lda * 2));
     // byte offset of each staged row (kOob when the row is masked)
     uint32_t src_off[PT];
     int src_row[PT];
@@ -289,7 +275,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
         src_off[i] = src_ok[i] ? (uint32_t)((int64_t)tok * a.lda * 2) : kOob;
       }
     }
-    const int nk = (Kp + kBK - 1) / kBK;
+    const int nk = (a.K + kBK - 1) / kBK;
     u32x4 stage[PT];
     auto load_stage = [&](int kt) {
       const int k = kt * kBK + ck * 8;
@@ -298,12 +284,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
         // staging step i covers rows RPI*i .. RPI*i + RPI - 1: all weight rows or all token rows
         const bool w_step = i < BN / RPI;
         if (ALIGNED) {
-          const uint32_t off = (k < Kp) ? src_off[i] + (uint32_t)(k * 2) : kOob;
+          const uint32_t off = (k < a.K) ? src_off[i] + (uint32_t)(k * 2) : kOob;
           stage[i] = w_step ? __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0)
                             : __builtin_amdgcn_raw_buffer_load_b128(rs_a, off, 0, 0);
         } else {
-          stage[i] = w_step ? load_chunk_slow(gW, a.ldw, src_row[i], src_ok[i], k, Kp)
-                            : load_chunk_slow(gA, a.lda, src_row[i], src_ok[i], k, Kp);
+          stage[i] = w_step ? load_chunk_slow(a.W, a.ldw, src_row[i], src_ok[i], k, a.K)
+                            : load_chunk_slow(a.A, a.lda, src_row[i], src_ok[i], k, a.K);
         }
       }
     };
@@ -354,7 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
     }
   }
 
-  store_tile<EPI, FT, MT, TM, TN>(a, gC, acc, m0, n0, wm, wn, lane);
+  store_tile<EPI, FT, MT, TM, TN>(a, a.C, acc, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -520,7 +506,7 @@ static hipError_t gemm_instance(const GemmArgs& a, hipStream_t s) {
   const int tiles_n = (a.N + out_per_tile - 1) / out_per_tile;
   const int nt = tiles_m * tiles_n;
   if (nt == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, ALIGNED>), dim3(nt, a.k_splits),
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, ALIGNED>), dim3(nt),
                      dim3(64 * WM * WN), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -534,7 +520,6 @@ static hipError_t gemm_dispatch_epi(const GemmArgs& a, hipStream_t s) {
     case EPI_GATED_F32_TO_F32:
       return gemm_instance<BM, BN, WM, WN, EPI_GATED_F32_TO_F32, ALIGNED>(a, s);
     case EPI_SWIGLU: return gemm_instance<BM, BN, WM, WN, EPI_SWIGLU, ALIGNED>(a, s);
-    case EPI_BIAS_TO_F32: return gemm_instance<BM, BN, WM, WN, EPI_BIAS_TO_F32, ALIGNED>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -559,24 +544,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const bool gated = a.epilogue == EPI_GATED_TO_F32 || a.epilogue == EPI_GATED_F32_IN ||
                      a.epilogue == EPI_GATED_F32_TO_F32;
   if (gated && ((a.N & 3) != 0 || (a.ldr & 3) != 0)) return hipErrorInvalidValue;
-  if (a.epilogue == EPI_BIAS_TO_F32 &&
-      ((a.N & 3) != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 15) != 0))
-    return hipErrorInvalidValue;
   // Buffer offsets are 32-bit: both operands must span less than 2 GiB.
   const int64_t w_rows = (a.epilogue == EPI_SWIGLU) ? (int64_t)a.up_offset + a.N : a.N;
   if (w_rows * a.ldw * 2 >= (int64_t)kOob || (int64_t)total_rows(a.rows) * a.lda * 2 >= (int64_t)kOob)
     return hipErrorInvalidValue;
-  if (a.k_splits != 1) {
-    // split reductions: fp32 partial outputs only, whole k-tiles per split, register-staged path
-    if (a.k_splits < 1 || a.k_splits > 64 || a.epilogue != EPI_BIAS_TO_F32 || a.bias != nullptr ||
-        a.K % (a.k_splits * kBK) != 0 || a.split_stride <= 0)
-      return hipErrorInvalidValue;
-    const bool al = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&
-                    ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) &&
-                    ((reinterpret_cast<uintptr_t>(a.W) & 15) == 0);
-    return al ? gemm_instance<128, 128, 2, 2, EPI_BIAS_TO_F32, true>(a, s)
-              : gemm_instance<128, 128, 2, 2, EPI_BIAS_TO_F32, false>(a, s);
-  }
   // a batch of requests: tiles of 256 (or 128) rows must not straddle two requests
   if (a.rows.batch > 1 && (a.rows.seq_pad % 256) != 0) return hipErrorInvalidValue;
   const bool aligned = (a.K % 8 == 0) && (a.lda % 8 == 0) && (a.ldw % 8 == 0) &&
@@ -610,7 +581,6 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       case EPI_GATED_F32_IN: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_IN>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_GATED_F32_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_dl<EPI_SWIGLU>, grid, block, 0, s, a, tiles_m, tiles_n); break;
-      case EPI_BIAS_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_BIAS_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -61,7 +61,7 @@ struct NormModArgs {
   float eps;
   int32_t x_f32;      // 1: x is fp32
   int64_t temb_stride;  // elements between the temb tables of successive requests (batch)
-  int32_t table_rows = 6;  // rows per modality of ada/temb: 6 in a block, 2 in the final layer
+  int32_t table_rows = 6;  // rows per modality of ada/temb (6 in a block)
 };
 hipError_t launch_norm_mod(const NormModArgs& a, hipStream_t s);
 
@@ -104,7 +104,6 @@ enum GemmEpilogue : int32_t {
   EPI_SWIGLU = 2,       // out (bf16) = silu(acc_gate) * acc_up, gate row n, up row up_offset + n
   EPI_GATED_F32_IN = 3, // out (bf16) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
   EPI_GATED_F32_TO_F32 = 4, // out (fp32) = resid (fp32) + (ada + temb)[mod(m)][chunk][n] * acc
-  EPI_BIAS_TO_F32 = 5,  // out (fp32) = acc + bias[mod(m)][n] (no bias: acc)
 };
 struct GemmArgs {
   const uint16_t* A;  // [rows, K] activations, row stride lda
@@ -121,27 +120,40 @@ struct GemmArgs {
   int32_t chunk;          // gated epilogues: modulation chunk of the gate
   int32_t up_offset;      // EPI_SWIGLU: first up row of W (= F)
   int64_t temb_stride;    // gated epilogues: elements between successive requests' temb tables
-  const float* bias = nullptr;  // EPI_BIAS_TO_F32: [2, N] per-modality bias, or null
-  // Split of the reduction (EPI_BIAS_TO_F32 without bias only): workgroup (tile, y) reduces over
-  // k in [y K / k_splits, (y + 1) K / k_splits) and writes its fp32 partial sums to
-  // C + y * split_stride.
-  int32_t k_splits = 1;
-  int64_t split_stride = 0;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
-// v[row][c] = sum over s of P[s][row][c] (s in order) + bias[mod(row)][c] for valid rows, 0 for
-// the tail: the reduction of a split-K projection. P: splits x [rows, C] fp32, split_stride
-// elements apart; C a multiple of 4.
-struct SplitReduceArgs {
-  const float* partials;
-  float* out;
-  const float* bias;  // [2, C] or null
-  RowLayout rows;
-  int32_t C, splits;
-  int64_t split_stride;
+// Velocity head (k_head.hip). k_head_prep folds the final table of both modalities:
+// mul[m][d] = gain[d] (1 + ada[m][1][d] + temb[m][1][d]) and
+// cst[m][c] = sum_d (ada[m][0][d] + temb[m][0][d]) w[m][c][d] + bias[m][c].
+struct HeadPrepArgs {
+  const float* gain;   // [D]
+  const float* ada;    // [2, 2, D]: row 0 shift, row 1 scale
+  const float* temb;   // [2, 2, D]
+  const uint16_t* w;   // [2, C, D] bf16
+  const float* bias;   // [2, C] or null
+  float* mul;          // out [2, D], 16-byte aligned
+  float* cst;          // out [2, C], 16-byte aligned
+  int32_t D, C;
 };
-hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t s);
+hipError_t launch_head_prep(const HeadPrepArgs& a, hipStream_t s);
+// k_head_proj, both modalities in one launch (m = 0 video, 1 audio): for each, over its own
+// rows, v[r] = rsqrt(mean(x[r]^2) + eps) ((x[r] * mul) w^T) + cst for r < valid, 0 for
+// valid <= r < rows; x * mul rounded to bf16 for the product.
+struct HeadProjArgs {
+  const void* x[2];       // [rows, D] bf16 (or fp32 with x_f32), row stride D, 16-byte aligned
+  float* v[2];            // [rows, C] fp32, row stride ldv, 16-byte aligned
+  const uint16_t* w[2];   // [C, D] bf16
+  const float* mul[2];    // [D], 16-byte aligned
+  const float* cst[2];    // [C], 16-byte aligned
+  int32_t rows[2], valid[2];
+  int32_t D, C;           // D a multiple of 64, at most 8192; C a multiple of 8
+  int64_t ldv;
+  float eps;
+  int32_t x_f32;
+  int32_t tiles0 = 0;     // set by the launcher: row tiles of modality 0
+};
+hipError_t launch_head_proj(const HeadProjArgs& a, hipStream_t s);
 
 // Flash-style attention over packed requests; element (b, i, h, d) of q/k/v at
 // b * batch_stride + i * row_stride + h * head_dim + d.

@@ -341,7 +341,9 @@ def configs_report(args):
         ms = gpu_ms(lambda: N.dit_velocity_head(dims, lay, head, th, xh, vh, ws, stream=stream))
         V, D, L = wl.n_valid, wl.hidden, wl.seq_pad
         min_bytes = 2.0 * V * D + 4.0 * L * C + 2.0 * 2 * C * D      # x in, v out, weights
-        run_bytes = min_bytes + 4.0 * V * D                           # + the bf16 h round trip
+        # the fused head reads x once and writes v once; the table fold adds the weights once more
+        # and a few tables of D and C floats
+        run_bytes = min_bytes + 2.0 * 2 * C * D + 4.0 * (7 * D + 4 * C)
         fl = 2.0 * V * D * C
         rec = {"workload": "head_32k", "kind": "velocity head", "valid": V, "seq_pad": L,
                "hidden": D, "channels": C, "gpu_ms": round(ms, 4),

@@ -29,8 +29,9 @@
  *    so each of these must span less than 2 GiB, else DIT_ERR_UNSUPPORTED: the weights
  *    w_qkv, w_gate_up, w_down; the block activations [rows, D] and the SwiGLU activations
  *    [rows, F] (rows = all rows of the call, batch * seq_pad for a batch); one request's
- *    q/k/v rows [seq_pad, 3D] (at hidden 3072: seq_pad <= 116,508); the head's input
- *    [seq_pad, D]. The workspace-size functions apply the same limits and return 0.
+ *    q/k/v rows [seq_pad, 3D] (at hidden 3072: seq_pad <= 116,508). The workspace-size
+ *    functions apply the same limits and return 0. (The velocity head addresses its input
+ *    per 64 or 128 rows, and one modality's weight [C, D] stays below 1 GiB: no limit.)
  *  - Errors: every argument is validated before anything is enqueued. On failure
  *    nothing is enqueued, a negative status is returned and dit_last_error() describes
  *    it. A launch failure reported by the runtime after enqueueing maps to
@@ -275,16 +276,19 @@ int denoise_loop_f32(const dit_dims* dims, const dit_layout* layout,
                      void* stream);
 
 /* Workspace of dit_velocity_head and dit_velocity_head_f32 for out_channels output channels:
- * the modulated norm (bf16 [seq_pad, D]) and, for out_channels <= 256 (the projection's
- * reduction is then split four ways), fp32 partial sums [4, seq_pad, out_channels]. Returns 0
- * with dit_last_error() set for invalid dims, layout or out_channels. */
+ * the final table folded per modality, fp32 mul [2, D] and cst [2, out_channels] (see
+ * dit_velocity_head); independent of seq_pad. Returns 0 with dit_last_error() set for invalid
+ * dims, layout or out_channels. */
 size_t dit_head_workspace_size(const dit_dims* dims, const dit_layout* layout,
                                int32_t out_channels);
 
 /* Velocity head ([P2] "Test Result", final AdaLN layer; [P1] section 1): for a valid row l of
  * modality m, h = x_l / sqrt(mean(x_l^2) + norm_eps) * norm_g * (1 + E[m][1]) + E[m][0] with
  * E = head->ada + temb (the same fused RMSNorm with indexed modulation as the block), then
- * v_l = h W_m^T + b_m in fp32 (h is rounded to bf16 for the product). Tail rows of v are 0.
+ * v_l = h W_m^T + b_m in fp32. Evaluated in one pass over x as
+ * v_l = r_l ((x_l * mul_m) W_m^T) + cst_m with r_l = 1 / sqrt(mean(x_l^2) + norm_eps),
+ * mul_m = norm_g * (1 + E[m][1]) and cst_m = E[m][0] W_m^T + b_m (fp32): x_l * mul_m is rounded
+ * to bf16 for the product, everything else stays fp32. Tail rows of v are 0.
  *   x: dev bf16 [seq_pad, D], the stack output, 16-byte aligned;
  *   temb: dev fp32 [n_mod, 2, D], the timestep part of the final table;
  *   v: dev fp32 [seq_pad, out_channels], 16-byte aligned.

@@ -34,7 +34,8 @@ hipError_t launch_norm_mod(const NormModArgs&, hipStream_t) { return stub_launch
 hipError_t launch_qk_norm_rope(const QkNormRopeArgs&, hipStream_t) { return stub_launch(); }
 hipError_t launch_step_update(const StepArgs&, hipStream_t) { return stub_launch(); }
 hipError_t launch_gemm(const GemmArgs&, hipStream_t) { return stub_launch(); }
-hipError_t launch_split_reduce(const SplitReduceArgs&, hipStream_t) { return stub_launch(); }
+hipError_t launch_head_prep(const HeadPrepArgs&, hipStream_t) { return stub_launch(); }
+hipError_t launch_head_proj(const HeadProjArgs&, hipStream_t) { return stub_launch(); }
 hipError_t launch_attention(const AttnArgs&, hipStream_t) { return stub_launch(); }
 }  // namespace avdit
 
@@ -304,13 +305,13 @@ static void other_entry_points() {
   dit_dims d = dims(256, 4, 64, 683);
   dit_layout hl{512, 96, 640, nullptr};
   const size_t need = dit_head_workspace_size(&d, &hl, 64);
-  EXPECT(need == (size_t)640 * 256 * 2 + (size_t)4 * 640 * 64 * 4);
+  EXPECT(need == (size_t)2 * 256 * 4 + (size_t)2 * 64 * 4);   // the folded table: mul, cst
   dit_head_weights hw{fp<const float>(1 << 12), fp<const float>(1 << 13),
                       fp<const uint16_t>(1 << 16), fp<const float>(1 << 14), 64};
   g_launches = 0;
   EXPECT(dit_velocity_head(&d, &hl, &hw, fp<float>(1 << 15), fp<uint16_t>(1 << 20),
                            fp<float>(1 << 24), fake(1ull << 40), need, nullptr) == DIT_OK);
-  EXPECT(g_launches == 4);   // norm, two projections, reduction
+  EXPECT(g_launches == 2);   // table fold, one projection over both modalities
   dit_head_weights bad = hw;
   bad.out_channels = 60;
   REJECT(dit_velocity_head(&d, &hl, &bad, fp<float>(1 << 15), fp<uint16_t>(1 << 20),
@@ -319,9 +320,10 @@ static void other_entry_points() {
   bad.norm_g = fp<const float>((1 << 12) + 4);
   REJECT(dit_velocity_head(&d, &hl, &bad, fp<float>(1 << 15), fp<uint16_t>(1 << 20),
                            fp<float>(1 << 24), fake(1ull << 40), need, nullptr), DIT_ERR_INVALID);
+  // the head reads its input through 64-bit addresses: long sequences have no span limit
   dit_dims wide = dims(8192, 64, 128, 8192);
   dit_layout long_l{131072, 0, 131072, nullptr};
-  EXPECT(dit_head_workspace_size(&wide, &long_l, 128) == 0);
+  EXPECT(dit_head_workspace_size(&wide, &long_l, 128) == (size_t)2 * 8192 * 4 + (size_t)2 * 128 * 4);
 }
 
 // dit_last_error is per thread: a failure on one thread is not seen, or cleared, by another.

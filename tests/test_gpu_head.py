@@ -52,9 +52,32 @@ def _gpu(env, wl, hp, x, temb, bias=True, f32=False, x_tail=None, ws_fill=None):
     v = torch.full((wl.seq_pad, C), float("nan"), dtype=torch.float32, device="cuda")
     N.dit_velocity_head(dims, lay, head, t, dx, v, ws, x_f32=f32)
     torch.cuda.synchronize()
-    h = dev.bf16_values_of(ws[: wl.seq_pad * wl.hidden * 2].view(torch.bfloat16)
-                           .view(wl.seq_pad, wl.hidden)).astype(np.float64)
-    return v.cpu().numpy().astype(np.float64), h
+    return v.cpu().numpy().astype(np.float64)
+
+
+def _at_kernel_rounding(wl, hp, x, temb, bias=True, f32=False):
+    """The head evaluated at the kernel's own rounding point, in float64 from there on: the folded
+    scale mul = g (1 + (ada + temb)) in float32 operations, x * mul multiplied in float32 and
+    rounded to bf16, then r (x * mul) W^T + (shift W^T + b) with r = 1 / sqrt(mean(x^2) + eps).
+    Same function as the oracle's head up to that one rounding of the product's input."""
+    import oracle as O
+    from audio_video_diffusion_dit_amd.inputs import bf16_bits, bf16_to_f32
+    p = hp.as_float()
+    x32 = (x if f32 else bf16_to_f32(x)).astype(np.float32)
+    x64 = x32.astype(np.float64)
+    ada32, t32 = hp.ada.astype(np.float32), np.asarray(temb, dtype=np.float32)
+    mod = O.row_modality(O.Layout(wl.n_video, wl.n_audio, wl.seq_pad))
+    r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=1) + 1e-6)
+    out = np.zeros((wl.seq_pad, p["w_out"].shape[1]))
+    for m in (0, 1):
+        sel = mod == m
+        mul32 = hp.norm_g.astype(np.float32) * (np.float32(1.0) + (ada32[m, 1] + t32[m, 1]))
+        a = bf16_to_f32(bf16_bits(x32[sel] * mul32)).astype(np.float64)
+        shift = (ada32[m, 0] + t32[m, 0]).astype(np.float64)
+        w = p["w_out"][m]
+        cst = O.linear(shift[None, :], w)[0] + (p["bias"][m] if bias else 0.0)
+        out[sel] = r[sel, None] * O.linear(a, w) + cst
+    return out
 
 
 def _oracle(wl, hp, x, temb, bias=True, f32=False, rows=None):
@@ -94,30 +117,20 @@ def test_head_against_oracle(env, D, nv, na, L, C, bias, f32):
     wl, hp, x, temb = _case(D, nv, na, L, C, seed=D + nv + C, f32=f32)
     V = wl.n_valid
     say(f"velocity head: D={D} video={nv} audio={na} L={L} C={C} bias={bias} fp32 x={f32}")
-    v, h = _gpu(env, wl, hp, x, temb, bias=bias, f32=f32, ws_fill=0x7F)
+    v = _gpu(env, wl, hp, x, temb, bias=bias, f32=f32, ws_fill=0x7F)
     ref = _oracle(wl, hp, x, temb, bias=bias, f32=f32)
     assert np.all(v[V:] == 0), "tail rows of v must be exactly 0"
     assert_close(v[:V], ref[:V], "velocity (end to end)")
-    # teacher-forced: the norm kernel against the oracle norm, the projection fed the GPU's h
-    from audio_video_diffusion_dit_amd.inputs import bf16_to_f32
-    p = hp.as_float()
-    xv = (x if f32 else bf16_to_f32(x)).astype(np.float64)
-    mod = O.row_modality(O.Layout(nv, na, L))
-    E = O.modulation_rows(p["ada"], temb)
-    h_ref = O.norm_modulate(xv, p["norm_g"], E, mod, O.HEAD_SHIFT, O.HEAD_SCALE, 1e-6)
-    assert_kernel_close(h[:V], h_ref[:V], "final norm+modulation")
-    proj = np.zeros_like(ref)
-    for m in (0, 1):
-        sel = mod == m
-        proj[sel] = O.linear(h[sel], p["w_out"][m]) + (p["bias"][m] if bias else 0.0)
-    assert_kernel_close(v[:V], proj[:V], "head projection + bias")
+    # teacher-forced: the fused kernel against the head at its own rounding point
+    tf = _at_kernel_rounding(wl, hp, x, temb, bias=bias, f32=f32)
+    assert_kernel_close(v[:V], tf[:V], "fused norm + modulation + projection")
 
 
 def test_head_tail_garbage_and_determinism(env):
     wl, hp, x, temb = _case(256, 100, 37, 200, 64, seed=3)
     say("velocity head: NaN in the input tail, two runs")
-    a, _ = _gpu(env, wl, hp, x, temb)
-    b, _ = _gpu(env, wl, hp, x, temb, x_tail=0x7FC0, ws_fill=0xFF)
+    a = _gpu(env, wl, hp, x, temb)
+    b = _gpu(env, wl, hp, x, temb, x_tail=0x7FC0, ws_fill=0xFF)
     assert np.array_equal(a, b)
 
 
@@ -127,7 +140,7 @@ def test_head_h3_scale_sampled_rows(env):
     from audio_video_diffusion_dit_amd import inputs as I
     wl, hp, x, temb = _case(3072, 30720, 2048, 32768, I.HEAD_CHANNELS, seed=9)
     say("velocity head at H3 scale: L=32768 D=3072 C=128")
-    v, _ = _gpu(env, wl, hp, x, temb)
+    v = _gpu(env, wl, hp, x, temb)
     rng = np.random.default_rng(10)
     rows = np.sort(np.concatenate([rng.choice(wl.n_valid, 60, replace=False),
                                    [0, wl.n_video - 1, wl.n_video, wl.n_valid - 1]]))
