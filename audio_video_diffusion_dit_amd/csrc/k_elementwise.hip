@@ -68,7 +68,9 @@ __device__ __forceinline__ void unpack_chunk(const RowChunk<F32IN>& r, float (&x
 template <int CPL, bool F32IN>  // CPL: 8-element chunks per lane, ceil(D / 512)
 __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform (readfirstlane): the per-request lookups of a batch then become scalar loads,
+  // whose wait does not drain the rows prefetched with vector loads
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int D = a.D;
   const int nchunk = D >> 3;
   const float inv_d = 1.0f / (float)D;
