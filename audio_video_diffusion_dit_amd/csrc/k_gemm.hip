@@ -1,9 +1,8 @@
 // bf16 MFMA GEMM for the block's projections: C[m][n] = sum_k A[m][k] * W[n][k], both operands
 // contiguous along k (activations [tokens, K], weights [out, in]), fp32 accumulation, with the
 // epilogue fused: plain store (QKV), gated residual (out-projection into the fp32 mid-block
-// residual, down-projection from it), SwiGLU over interleaved gate/up weight rows (gate/up
-// projection; TeleFuser PR #23, "Changes Made": fused SwiGLU), or an fp32 store with a
-// per-modality bias (the velocity head's output projection).
+// residual, down-projection from it), or SwiGLU over interleaved gate/up weight rows (gate/up
+// projection; TeleFuser PR #23, "Changes Made": fused SwiGLU).
 //
 // Design for gfx950:
 //  * WM x WN wave64s per workgroup; each wave owns a (BN/WN features) x (BM/WM tokens)
@@ -381,6 +380,151 @@ __device__ __forceinline__ void dl_b128(uint32_t lds_base, uint32_t voffset, i32
 // chunk (8 even and 8 odd rows) land on 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int dl_swz(int r) { return (r >> 1) & 7; }
 
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+
+// Epilogue of the direct-to-LDS kernel, staged through the LDS ring (free once every wave has
+// passed the barrier at its top). In the MFMA layout a lane holds 4 features of one token, so a
+// store instruction straight from the accumulators writes 8 or 16 bytes into each of 32 token
+// rows; here each wave writes its 128 tokens x 64 features of fp32 accumulators into a private
+// 16 KB region (half of them per pass) and reads them back row-major, 16 lanes per token row
+// (8 for SwiGLU's 32 output features), so that every global load and store instruction covers
+// whole 128- or 256-byte row segments of 4 or 8 rows. The gated epilogues issue all their
+// residual and gate loads before the first store: loads and stores share one completion
+// counter, so a load issued after a store would be waited for together with that store.
+// Same values and roundings as the register epilogue: acc (fp32), then silu(g) u, or
+// resid + gate acc (fmaf), or the plain value, rounded once to the output type.
+template <int EPI>
+__device__ __forceinline__ void store_tile_staged(const GemmArgs& a, f32x16 (&acc)[2][4], int m0,
+                                                  int n0, int wm, int wn, int lane,
+                                                  lds_char_t* region) {
+  constexpr int TM = 128;                                  // tokens per wave
+  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
+                         (EPI == EPI_GATED_F32_TO_F32);
+  constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
+  constexpr bool RESID_F32 = (EPI == EPI_GATED_F32_IN) || (EPI == EPI_GATED_F32_TO_F32);
+  constexpr int OUT_T = (EPI == EPI_SWIGLU) ? 1 : 2;      // 32-feature output sub-tiles
+  constexpr int OF = OUT_T * 32;                           // output features of the wave
+  constexpr int LR = OF / 4;                               // lanes per token row
+  constexpr int RI = 64 / LR;                              // token rows per step
+  constexpr int TP = 128 / OF;                             // 32-row blocks per pass (16 KB)
+  constexpr int NP = 4 / TP;                               // passes
+  constexpr int RB = OF * 4;                               // bytes per staged row
+  constexpr int SPP = TP * 32 / RI;                        // steps per pass
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int rsub = lane / LR, q = lane % LR;
+  const int rows_total = total_rows(a.rows);
+  const int fb = n0 + wn * OF + 4 * q;                     // this lane's 4 output features
+  const int tok0 = m0 + wm * TM;
+  // A tile never straddles two requests: the request, its first row and its bounds are uniform.
+  int req = 0, base = 0, nvalid = a.rows.n_valid, nvideo = a.rows.n_video;
+  if (a.rows.batch > 1) {
+    req = m0 / a.rows.seq_pad;
+    base = req * a.rows.seq_pad;
+    nvalid = a.rows.req_valid[req];
+    nvideo = a.rows.req_video[req];
+  }
+  // Bank-conflict-free staging: 16-byte chunk c of row r sits at chunk c ^ sw(r); 256-byte rows
+  // span all 64 banks (sw = r mod 16), 128-byte rows pair up (sw = (r >> 1) mod 8).
+  auto sw = [](int r) __attribute__((always_inline)) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
+
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[0][t][e] = silu_mul(acc[0][t][e], acc[1][t][e]);
+  }
+  auto stage = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < TP; ++tt) {
+      const int row = tt * 32 + l32;
+#pragma unroll
+      for (int f = 0; f < OUT_T; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 8 * f + 2 * j + hh;
+          const f32x4 v = {acc[f][p * TP + tt][4 * j], acc[f][p * TP + tt][4 * j + 1],
+                           acc[f][p * TP + tt][4 * j + 2], acc[f][p * TP + tt][4 * j + 3]};
+          *reinterpret_cast<lds_f32x4_t*>(region + row * RB + ((c ^ sw(row)) << 4)) = v;
+        }
+    }
+  };
+  __syncthreads();  // every wave is done with the ring's fragments
+  stage(0);
+
+  // gated: every residual the wave reads, then the gate terms (ada, temb) of both modalities
+  // for the lane's features, all in flight before the first store; the gate sum ada + temb is
+  // formed at its first use, so that no wait separates the loads
+  f32x4 rv[NP][SPP];
+  float4 ga[2], gt[2];
+  if constexpr (GATED) {
+    const int fc = fb < a.N ? fb : a.N - 4;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int st = 0; st < SPP; ++st) {
+        int tok = tok0 + p * TP * 32 + st * RI + rsub;
+        tok = tok < rows_total ? tok : rows_total - 1;
+        if constexpr (RESID_F32) {
+          const float4 r4 = *reinterpret_cast<const float4*>(
+              static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fc);
+          rv[p][st] = f32x4{r4.x, r4.y, r4.z, r4.w};
+        } else {
+          const u32x2 rr = *reinterpret_cast<const u32x2*>(
+              static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fc);
+          rv[p][st] = f32x4{bf_lo(rr.x), bf_hi(rr.x), bf_lo(rr.y), bf_hi(rr.y)};
+        }
+      }
+#pragma unroll
+    for (int mod = 0; mod < 2; ++mod) {
+      const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fc;
+      ga[mod] = *reinterpret_cast<const float4*>(a.ada + goff);
+      gt[mod] = *reinterpret_cast<const float4*>(a.temb + req * a.temb_stride + goff);
+    }
+  }
+
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (p > 0) stage(p);  // the wave's own reads of pass p - 1 precede these writes (LDS order)
+#pragma unroll
+    for (int st = 0; st < SPP; ++st) {
+      const int row = st * RI + rsub;
+      const f32x4 v = *reinterpret_cast<lds_f32x4_t*>(region + row * RB + ((q ^ sw(row)) << 4));
+      const int tok = tok0 + p * TP * 32 + row;
+      if (tok >= rows_total || fb >= a.N) continue;
+      const int i = tok - base;
+      float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (i < nvalid) {
+        if constexpr (GATED) {
+          const float4 g4 = i < nvideo ? make_float4(ga[0].x + gt[0].x, ga[0].y + gt[0].y,
+                                                     ga[0].z + gt[0].z, ga[0].w + gt[0].w)
+                                       : make_float4(ga[1].x + gt[1].x, ga[1].y + gt[1].y,
+                                                     ga[1].z + gt[1].z, ga[1].w + gt[1].w);
+          o[0] = fmaf(g4.x, v[0], rv[p][st][0]);
+          o[1] = fmaf(g4.y, v[1], rv[p][st][1]);
+          o[2] = fmaf(g4.z, v[2], rv[p][st][2]);
+          o[3] = fmaf(g4.w, v[3], rv[p][st][3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = v[e];
+        }
+      }
+      if constexpr (OUT_F32) {
+        float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
+        *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
+        if (fb + 4 <= a.N) {
+          *reinterpret_cast<u32x2*>(crow + fb) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (fb + e < a.N) crow[fb + e] = to_bf16(o[e]);
+        }
+      }
+    }
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int tiles_n) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
@@ -496,7 +640,9 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
     }
     mfmas((KS - 1) & 1);
   }
-  store_tile<EPI, FT, MT, TM, TN>(a, a.C, acc, m0, n0, wm, wn, lane);
+  static_assert(FT == 2 && MT == 4 && TM == 128 && STAGES * kDlStageBytes == NW * 16384,
+                "staged epilogue: 128 x 64 accumulators and 16 KB of the ring per wave");
+  store_tile_staged<EPI>(a, acc, m0, n0, wm, wn, lane, (lds_char_t*)(lds_ring) + wave * 16384);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
