@@ -21,6 +21,8 @@
 //    length, so keys past it read as zero. Tiles are double buffered with one barrier per
 //    tile, and the next tile's loads are in flight during the current tile's math. The key
 //    loop is unrolled by two so that both LDS buffers are addressed with immediate offsets.
+//    The first tiles are issued before the Q fragments and the gains are loaded, so that the
+//    prologue waits for memory once rather than once per operand.
 //  * Only the last partial tile (and, in fixed-valid mode, the tiles past the valid length)
 //    run the masking code.
 //  * Softmax shift: q and k of the DiT block come out of the per-head Q/K RMSNorm, so every
@@ -163,21 +165,6 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
     return;
   }
 
-  const int my_q = q0 + wave * 32 + l32;
-  const float c = a.scale_log2;
-  bf16x8 qf[QS];
-#pragma unroll
-  for (int s = 0; s < QS; ++s) {
-    u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (my_q < V) w = *reinterpret_cast<const u32x4*>(Q + (int64_t)my_q * a.row_stride + (2 * s + hh) * 8);
-    qf[s] = __builtin_bit_cast(bf16x8, w);
-  }
-  // Consume the Q fragments once here: the compiler then places its wait for these loads before
-  // the key loop instead of at their first use inside it, where the same counter would also
-  // wait for the K/V prefetch in flight (the LDS-destination loads are invisible to it).
-#pragma unroll
-  for (int s = 0; s < QS; ++s) asm volatile("" ::"v"(qf[s]));
-
   // ---- global -> LDS staging: wave w's i-th load fills 16-byte slots (kNW i + w) * 64 + lane of
   // a tile, i.e. row p / NC and physical chunk p % NC of slot p; the lane fetches the logical
   // chunk that the swizzle places there. Keys >= V read as zero (resource range). ----
@@ -210,7 +197,96 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
       dma_b128(lds0 + buf * BUFB + VOFF + i * (kNW * 1024), g + ov, rs_v);
     }
   };
+  auto load_k = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t g = (uint32_t)kt * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t ok = (DH == 128) ? goff_k[0] + i * gstep : goff_k[i % GK];
+      dma_b128(lds0 + buf * BUFB + i * (kNW * 1024), g + ok, rs_k);
+    }
+  };
+  auto load_v = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t g = (uint32_t)kt * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t ov = (DH == 128) ? goff_v[0] + i * gstep : goff_v[i % GK];
+      dma_b128(lds0 + buf * BUFB + VOFF + i * (kNW * 1024), g + ov, rs_v);
+    }
+  };
 
+  const int key_end = a.fixed_valid ? L : V;
+  const int nkt = (key_end + kKB - 1) / kKB;
+  const int n_full = V / kKB;  // tiles whose 64 keys are all valid
+
+  // Prologue in one memory round trip: the first K and V tiles and the next K tile are issued
+  // into their buffers before the Q fragments and the gains are loaded; the compiler's wait for
+  // those (before the key loop) then also covers the tiles, since loads complete in issue order.
+  // (The paths with a running or fixed shift load K and V of tile 1 again at their first tile:
+  // the same bytes into the same place, before any wave reads them.)
+  load_tile(0, 0);
+  if (nkt > 1) load_k(1, 1);
+  // the Q/K RMSNorm gains (for the logit bound below), lane-strided
+  const bool has_gains = a.q_gain != nullptr && a.k_gain != nullptr;
+  float graw[2][DH / 64] = {};
+  if (has_gains) {
+#pragma unroll
+    for (int r = 0; r < DH / 64; ++r) {
+      graw[0][r] = a.q_gain[lane + 64 * r];
+      graw[1][r] = a.k_gain[lane + 64 * r];
+    }
+  }
+  const int my_q = q0 + wave * 32 + l32;
+  const float c = a.scale_log2;
+  bf16x8 qf[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (my_q < V) w = *reinterpret_cast<const u32x4*>(Q + (int64_t)my_q * a.row_stride + (2 * s + hh) * 8);
+    qf[s] = __builtin_bit_cast(bf16x8, w);
+  }
+  // Consume the Q fragments and the gains once here: the compiler then places its wait for these
+  // loads here, where it also covers the tiles issued before them, instead of at their first use
+  // inside the key loop, where the same counter would also wait for the K/V prefetch in flight
+  // (the LDS-destination loads are invisible to it).
+#pragma unroll
+  for (int s = 0; s < QS; ++s) asm volatile("" ::"v"(qf[s]));
+#pragma unroll
+  for (int r = 0; r < DH / 64; ++r) asm volatile("" ::"v"(graw[0][r]), "v"(graw[1][r]));
+
+
+  // Logit bound from the Q/K RMSNorm gains: a normalised head vector has norm below sqrt(Dh),
+  // so |q.k| < max|gq| max|gk| Dh; the factor 1 + 2^-6 covers the bf16 roundings of q, k and
+  // q c. In log2 units (times c): up to 30, every probability exp2(s c) lies in [2^-31, 2^31]
+  // (P V sums stay far from fp32 overflow); up to 60, exp2(s c - bound) lies in [2^-121, 1].
+  // Both are normal in fp32 and bf16, and no running maximum is needed.
+  float bound = INFINITY;
+  if (has_gains) {
+    float gq = 0.0f, gk = 0.0f;
+#pragma unroll
+    for (int r = 0; r < DH / 64; ++r) {
+      gq = fmaxf(gq, fabsf(graw[0][r]));
+      gk = fmaxf(gk, fabsf(graw[1][r]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      gq = fmaxf(gq, __shfl_xor(gq, o, 64));
+      gk = fmaxf(gk, __shfl_xor(gk, o, 64));
+    }
+    bound = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+        int, gq * gk * (float)DH * c * (1.0f + 1.0f / 64.0f))));
+  }
+  // 2: no shift, 1: shift by the bound, 0: online maximum (also for an infinite or NaN bound)
+  const int shift_mode = bound <= 30.0f ? 2 : (bound <= 60.0f ? 1 : 0);
+  if (shift_mode == 2) {
+    // fold c into the Q fragments: the score MFMAs then yield logits in log2 units
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      bf16x8 scaled;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) scaled[e] = (__bf16)((float)qf[s][e] * c);
+      qf[s] = scaled;
+    }
+  }
   // ---- per-lane LDS read addresses (byte offsets inside buffer 0) ----
   // K fragment of score k-step s, key half h2: row 32 h2 + l32, logical chunk 2 s + hh. At
   // head_dim 128 the swizzle ignores h2, which then only adds 32 rows.
@@ -247,43 +323,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  // Logit bound from the Q/K RMSNorm gains: a normalised head vector has norm below sqrt(Dh),
-  // so |q.k| < max|gq| max|gk| Dh; the factor 1 + 2^-6 covers the bf16 roundings of q, k and
-  // q c. In log2 units (times c): up to 30, every probability exp2(s c) lies in [2^-31, 2^31]
-  // (P V sums stay far from fp32 overflow); up to 60, exp2(s c - bound) lies in [2^-121, 1].
-  // Both are normal in fp32 and bf16, and no running maximum is needed.
-  float bound = INFINITY;
-  if (a.q_gain != nullptr && a.k_gain != nullptr) {
-    float gq = 0.0f, gk = 0.0f;
-    for (int i = lane; i < DH; i += 64) {
-      gq = fmaxf(gq, fabsf(a.q_gain[i]));
-      gk = fmaxf(gk, fabsf(a.k_gain[i]));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      gq = fmaxf(gq, __shfl_xor(gq, o, 64));
-      gk = fmaxf(gk, __shfl_xor(gk, o, 64));
-    }
-    bound = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-        int, gq * gk * (float)DH * c * (1.0f + 1.0f / 64.0f))));
-  }
-  // 2: no shift, 1: shift by the bound, 0: online maximum (also for an infinite or NaN bound)
-  const int shift_mode = bound <= 30.0f ? 2 : (bound <= 60.0f ? 1 : 0);
-  if (shift_mode == 2) {
-    // fold c into the Q fragments: the score MFMAs then yield logits in log2 units
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      bf16x8 scaled;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) scaled[e] = (__bf16)((float)qf[s][e] * c);
-      qf[s] = scaled;
-    }
-  }
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
-
-  const int key_end = a.fixed_valid ? L : V;
-  const int nkt = (key_end + kKB - 1) / kKB;
-  const int n_full = V / kKB;  // tiles whose 64 keys are all valid
 
   auto tile = [&](auto mode_c, auto masked_c, auto buf_c, int kt) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
@@ -427,22 +467,6 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
   // staged one tile apart: while iteration j runs, K(j + 1) and V(j) are in flight into the
   // halves of the double buffer that iteration j - 1 finished reading (K(t) and V(t) live in
   // buffer t & 1). ----
-  auto load_k = [&](int kt, int buf) __attribute__((always_inline)) {
-    const uint32_t g = (uint32_t)kt * tile_bytes;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const uint32_t ok = (DH == 128) ? goff_k[0] + i * gstep : goff_k[i % GK];
-      dma_b128(lds0 + buf * BUFB + i * (kNW * 1024), g + ok, rs_k);
-    }
-  };
-  auto load_v = [&](int kt, int buf) __attribute__((always_inline)) {
-    const uint32_t g = (uint32_t)kt * tile_bytes;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const uint32_t ov = (DH == 128) ? goff_v[0] + i * gstep : goff_v[i % GK];
-      dma_b128(lds0 + buf * BUFB + VOFF + i * (kNW * 1024), g + ov, rs_v);
-    }
-  };
   constexpr int NS = 2 * QS;            // score MFMAs per tile
   constexpr int NP = 4 * DT;            // P V MFMAs per tile
   // 64 VALU operations per tile (32 exps, 16 packs, 16 row-sum dots): 4 before the first slot,
@@ -574,11 +598,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
   };
   auto sweep_pipelined = [&]() __attribute__((always_inline)) {
     f32x16 sA[2], sB[2];
-    load_k(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (nkt > 1) load_k(1, 1);
-    load_v(0, 0);
     s_only(0, sA);
     if (0 >= n_full) mask_tile(sA, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -605,7 +626,6 @@ __global__ __launch_bounds__(64 * kNW, 1) void k_attn(AttnArgs a) {
   if (shift_mode == 2) {
     sweep_pipelined();
   } else {
-    load_tile(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (shift_mode == 1)
