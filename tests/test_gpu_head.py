@@ -107,8 +107,8 @@ def _oracle(wl, hp, x, temb, bias=True, f32=False, rows=None):
     (512, 300, 0, 512, 128, True, False),     # video only
     (512, 0, 250, 300, 136, True, True),      # audio only, fp32 input, C not a tile multiple
     (256, 512, 96, 640, 64, True, True),
-    # unsplit projection with the bias in the GEMM epilogue: more than 256 channels, and a hidden
-    # size that is not a multiple of 256 (5 x 64)
+    # three channel tiles, the last one partial (264 = 2 x 128 + 8), and a hidden size of five
+    # 64-wide k-tiles (320)
     (256, 300, 44, 384, 264, True, False),
     (320, 200, 50, 256, 64, True, False),
 ])
