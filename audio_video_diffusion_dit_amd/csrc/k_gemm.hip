@@ -429,9 +429,14 @@ __device__ __forceinline__ void store_tile_staged(const GemmArgs& a, f32x16 (&ac
     nvalid = a.rows.req_valid[req];
     nvideo = a.rows.req_video[req];
   }
-  // Bank-conflict-free staging: 16-byte chunk c of row r sits at chunk c ^ sw(r); 256-byte rows
-  // span all 64 banks (sw = r mod 16), 128-byte rows pair up (sw = (r >> 1) mod 8).
-  auto sw = [](int r) __attribute__((always_inline)) { return RB == 256 ? (r & 15) : ((r >> 1) & 7); };
+  // Bank-conflict-free staging: 16-byte chunk c of row r sits at chunk c ^ sw(r), so that the 8
+  // (or 16) lanes that the LDS serves together, consecutive rows at one chunk when writing and
+  // the chunks of one or two rows when reading, fall on distinct 16-byte bank groups of 128 (or
+  // 256) bytes: sw = r mod 16 for 256-byte rows; for 128-byte rows sw = (r mod 8) ^ (r / 8 mod 2),
+  // a permutation on every 8 aligned rows that also separates the even (and the odd) rows of 16.
+  auto sw = [](int r) __attribute__((always_inline)) {
+    return RB == 256 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+  };
 
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
