@@ -86,117 +86,153 @@ __device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_
   tile_n = in_group / gm;
 }
 
-// Fused epilogue of one wave's accumulator block: lane (l32, hh) holds features fb..fb+3 of
-// token m0 + wm TM + 32 t + l32 in acc[f][t][4 j .. 4 j + 3], fb = n0 + wn (OUT_T 32) + 32 f +
-// 8 j + 4 hh (SwiGLU pairs gate sub-tile 2 f with up sub-tile 2 f + 1). Invalid rows (at or past
-// a request's valid length) are written 0, rows past the last request are not written.
-template <int EPI, int FT, int MT, int TM, int TN>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, void* C, f32x16 (&acc)[FT][MT], int m0,
-                                           int n0, int wm, int wn, int lane) {
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-  const int rows_total = total_rows(a.rows);
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+
+// Fused epilogue, staged through the LDS (free once every wave has passed the barrier at its
+// top). In the MFMA layout lane (l32, hh) holds features 32 f + 8 j + 4 hh .. + 3 of token
+// 32 t + l32 of its wave's block in acc[f][t][4 j .. 4 j + 3] (SwiGLU pairs gate sub-tile 0 with
+// up sub-tile 1), so a store instruction straight from the accumulators writes 8 or 16 bytes into
+// each of 32 token rows. Here each wave writes its 32 MT tokens x 64 features of fp32
+// accumulators into a private 16 KB region (64 tokens per pass) and reads them back row-major, 16
+// lanes per token row (8 for SwiGLU's 32 output features), so that every global load and store
+// instruction covers whole 128- or 256-byte row segments of 4 or 8 rows. Invalid rows (at or
+// past a request's valid length) are written 0, rows past the last request are not written. The gated epilogues issue all their
+// residual and gate loads before the first store: loads and stores share one completion
+// counter, so a load issued after a store would be waited for together with that store.
+// Same values and roundings as the register epilogue: acc (fp32), then silu(g) u, or
+// resid + gate acc (fmaf), or the plain value, rounded once to the output type.
+template <int EPI, int MT>
+__device__ __forceinline__ void store_tile_staged(const GemmArgs& a, f32x16 (&acc)[2][MT], int m0,
+                                                  int n0, int wm, int wn, int lane,
+                                                  lds_char_t* region) {
+  constexpr int TM = 32 * MT;                              // tokens per wave
   constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
                          (EPI == EPI_GATED_F32_TO_F32);
   constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
-  constexpr int OUT_T = (EPI == EPI_SWIGLU) ? FT / 2 : FT;
-  // Gate values (ada + temb of the row's request and modality) of this lane's features. When all
-  // rows of the wave's token range belong to one request and one modality (every tile but the
-  // one holding a video/audio or request boundary), they are loaded once for the whole range
-  // instead of once per row: wave-uniform test on the range's first and last row.
-  float gv[OUT_T][4][4];
-  bool gate_once = false;
-  auto load_gate = [&](int mod, int req) __attribute__((always_inline)) {
-#pragma unroll
-    for (int f = 0; f < OUT_T; ++f) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int fb0 = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
-        const int fb = fb0 < a.N ? fb0 : a.N - 4;
-        const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fb;
-        const float4 ga = *reinterpret_cast<const float4*>(a.ada + goff);
-        const float4 gt = *reinterpret_cast<const float4*>(a.temb + req * a.temb_stride + goff);
-        gv[f][j][0] = ga.x + gt.x; gv[f][j][1] = ga.y + gt.y;
-        gv[f][j][2] = ga.z + gt.z; gv[f][j][3] = ga.w + gt.w;
-      }
-    }
-  };
-  if constexpr (GATED) {
-    const int tok0 = m0 + wm * TM;
-    if (tok0 < rows_total) {
-      const int tok1 = (tok0 + TM <= rows_total ? tok0 + TM : rows_total) - 1;
-      const RowInfo r0 = row_info(a.rows, tok0), r1 = row_info(a.rows, tok1);
-      gate_once = r0.req == r1.req && r0.mod == r1.mod;
-      if (gate_once) load_gate(r0.mod, r0.req);
-    }
+  constexpr bool RESID_F32 = (EPI == EPI_GATED_F32_IN) || (EPI == EPI_GATED_F32_TO_F32);
+  constexpr int OUT_T = (EPI == EPI_SWIGLU) ? 1 : 2;      // 32-feature output sub-tiles
+  constexpr int OF = OUT_T * 32;                           // output features of the wave
+  constexpr int LR = OF / 4;                               // lanes per token row
+  constexpr int RI = 64 / LR;                              // token rows per step
+  constexpr int TP = (128 / OF) < MT ? (128 / OF) : MT;    // 32-row blocks per pass (<= 16 KB)
+  constexpr int NP = MT / TP;                              // passes
+  static_assert(MT % TP == 0, "whole passes");
+  constexpr int RB = OF * 4;                               // bytes per staged row
+  constexpr int SPP = TP * 32 / RI;                        // steps per pass
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int rsub = lane / LR, q = lane % LR;
+  const int rows_total = total_rows(a.rows);
+  const int fb = n0 + wn * OF + 4 * q;                     // this lane's 4 output features
+  const int tok0 = m0 + wm * TM;
+  // A tile never straddles two requests: the request, its first row and its bounds are uniform.
+  int req = 0, base = 0, nvalid = a.rows.n_valid, nvideo = a.rows.n_video;
+  if (a.rows.batch > 1) {
+    req = m0 / a.rows.seq_pad;
+    base = req * a.rows.seq_pad;
+    nvalid = a.rows.req_valid[req];
+    nvideo = a.rows.req_video[req];
   }
+  // Bank-conflict-free staging: 16-byte chunk c of row r sits at chunk c ^ sw(r), so that the 8
+  // (or 16) lanes that the LDS serves together, consecutive rows at one chunk when writing and
+  // the chunks of one or two rows when reading, fall on distinct 16-byte bank groups of 128 (or
+  // 256) bytes: sw = r mod 16 for 256-byte rows; for 128-byte rows sw = (r mod 8) ^ (r / 8 mod 2),
+  // a permutation on every 8 aligned rows that also separates the even (and the odd) rows of 16.
+  auto sw = [](int r) __attribute__((always_inline)) {
+    return RB == 256 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+  };
+
+  if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int tok = m0 + wm * TM + t * 32 + l32;
-    if (tok >= rows_total) continue;
-    const RowInfo ri = row_info(a.rows, tok);
-    const bool valid = ri.valid;
-    const int mod = ri.mod;
-    // Gated epilogues: every load of this token row (residual and gate values) is issued before
-    // the row's first store, so they share one memory round trip. The compiler cannot prove that
-    // the output stores do not alias them and would otherwise keep each load group behind the
-    // previous store. Feature offsets past N are clamped to a valid address (the values are
-    // then discarded).
-    float rv[OUT_T][4][4];
-    if constexpr (GATED) {
-      if (!gate_once) load_gate(mod, ri.req);
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int f = 0; f < OUT_T; ++f) {
+      for (int e = 0; e < 16; ++e) acc[0][t][e] = silu_mul(acc[0][t][e], acc[1][t][e]);
+  }
+  auto stage = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < TP; ++tt) {
+      const int row = tt * 32 + l32;
+#pragma unroll
+      for (int f = 0; f < OUT_T; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int fb0 = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
-          const int fb = fb0 < a.N ? fb0 : a.N - 4;
-          if constexpr (EPI == EPI_GATED_TO_F32) {
-            const u32x2 rr = *reinterpret_cast<const u32x2*>(
-                static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fb);
-            rv[f][j][0] = bf_lo(rr.x); rv[f][j][1] = bf_hi(rr.x);
-            rv[f][j][2] = bf_lo(rr.y); rv[f][j][3] = bf_hi(rr.y);
-          } else {
-            const float4 rr = *reinterpret_cast<const float4*>(
-                static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fb);
-            rv[f][j][0] = rr.x; rv[f][j][1] = rr.y; rv[f][j][2] = rr.z; rv[f][j][3] = rr.w;
-          }
+          const int c = 8 * f + 2 * j + hh;
+          const f32x4 v = {acc[f][p * TP + tt][4 * j], acc[f][p * TP + tt][4 * j + 1],
+                           acc[f][p * TP + tt][4 * j + 2], acc[f][p * TP + tt][4 * j + 3]};
+          *reinterpret_cast<lds_f32x4_t*>(region + row * RB + ((c ^ sw(row)) << 4)) = v;
+        }
+    }
+  };
+  __syncthreads();  // every wave is done with the ring's fragments
+  stage(0);
+
+  // gated: every residual the wave reads, then the gate terms (ada, temb) of both modalities
+  // for the lane's features, all in flight before the first store; the gate sum ada + temb is
+  // formed at its first use, so that no wait separates the loads
+  f32x4 rv[NP][SPP];
+  float4 ga[2], gt[2];
+  if constexpr (GATED) {
+    const int fc = fb < a.N ? fb : a.N - 4;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int st = 0; st < SPP; ++st) {
+        int tok = tok0 + p * TP * 32 + st * RI + rsub;
+        tok = tok < rows_total ? tok : rows_total - 1;
+        if constexpr (RESID_F32) {
+          const float4 r4 = *reinterpret_cast<const float4*>(
+              static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fc);
+          rv[p][st] = f32x4{r4.x, r4.y, r4.z, r4.w};
+        } else {
+          const u32x2 rr = *reinterpret_cast<const u32x2*>(
+              static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fc);
+          rv[p][st] = f32x4{bf_lo(rr.x), bf_hi(rr.x), bf_lo(rr.y), bf_hi(rr.y)};
         }
       }
+#pragma unroll
+    for (int mod = 0; mod < 2; ++mod) {
+      const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fc;
+      ga[mod] = *reinterpret_cast<const float4*>(a.ada + goff);
+      gt[mod] = *reinterpret_cast<const float4*>(a.temb + req * a.temb_stride + goff);
     }
+  }
+
 #pragma unroll
-    for (int f = 0; f < OUT_T; ++f) {
+  for (int p = 0; p < NP; ++p) {
+    if (p > 0) stage(p);  // the wave's own reads of pass p - 1 precede these writes (LDS order)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int fb = n0 + wn * (OUT_T * 32) + f * 32 + 8 * j + 4 * hh;
-        if (fb >= a.N) continue;
-        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (valid) {
-          if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              o[i] = silu_mul(acc[2 * f][t][4 * j + i], acc[2 * f + 1][t][4 * j + i]);
-          } else if constexpr (GATED) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = fmaf(gv[f][j][i], acc[f][t][4 * j + i], rv[f][j][i]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = acc[f][t][4 * j + i];
-          }
-        }
-        if constexpr (OUT_F32) {
-          float* crow = static_cast<float*>(C) + (int64_t)tok * a.ldc;
-          *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
+    for (int st = 0; st < SPP; ++st) {
+      const int row = st * RI + rsub;
+      const f32x4 v = *reinterpret_cast<lds_f32x4_t*>(region + row * RB + ((q ^ sw(row)) << 4));
+      const int tok = tok0 + p * TP * 32 + row;
+      if (tok >= rows_total || fb >= a.N) continue;
+      const int i = tok - base;
+      float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (i < nvalid) {
+        if constexpr (GATED) {
+          const float4 g4 = i < nvideo ? make_float4(ga[0].x + gt[0].x, ga[0].y + gt[0].y,
+                                                     ga[0].z + gt[0].z, ga[0].w + gt[0].w)
+                                       : make_float4(ga[1].x + gt[1].x, ga[1].y + gt[1].y,
+                                                     ga[1].z + gt[1].z, ga[1].w + gt[1].w);
+          o[0] = fmaf(g4.x, v[0], rv[p][st][0]);
+          o[1] = fmaf(g4.y, v[1], rv[p][st][1]);
+          o[2] = fmaf(g4.z, v[2], rv[p][st][2]);
+          o[3] = fmaf(g4.w, v[3], rv[p][st][3]);
         } else {
-          uint16_t* crow = static_cast<uint16_t*>(C) + (int64_t)tok * a.ldc;
-          if (fb + 4 <= a.N) {
-            *reinterpret_cast<u32x2*>(crow + fb) =
-                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-          } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (fb + i < a.N) crow[fb + i] = to_bf16(o[i]);
-          }
+          for (int e = 0; e < 4; ++e) o[e] = v[e];
+        }
+      }
+      if constexpr (OUT_F32) {
+        float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
+        *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
+        if (fb + 4 <= a.N) {
+          *reinterpret_cast<u32x2*>(crow + fb) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (fb + e < a.N) crow[fb + e] = to_bf16(o[e]);
         }
       }
     }
@@ -339,7 +375,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
     }
   }
 
-  store_tile<EPI, FT, MT, TM, TN>(a, a.C, acc, m0, n0, wm, wn, lane);
+  static_assert(FT == 2 && sizeof(lds) == WM * WN * 16384,
+                "staged epilogue: 64 features per wave and 16 KB of the LDS per wave");
+  store_tile_staged<EPI, MT>(a, acc, m0, n0, wm, wn, lane, (lds_char_t*)(&lds[0][0]) + wave * 16384);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -385,156 +423,6 @@ __device__ __forceinline__ void dl_b128(uint32_t lds_base, uint32_t voffset, i32
 // Chunk swizzle of a 128-byte LDS row: the 16 rows that one group of lanes reads at a logical
 // chunk (8 even and 8 odd rows) land on 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int dl_swz(int r) { return (r >> 1) & 7; }
-
-typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
-
-// Epilogue of the direct-to-LDS kernel, staged through the LDS ring (free once every wave has
-// passed the barrier at its top). In the MFMA layout a lane holds 4 features of one token, so a
-// store instruction straight from the accumulators writes 8 or 16 bytes into each of 32 token
-// rows; here each wave writes its 128 tokens x 64 features of fp32 accumulators into a private
-// 16 KB region (half of them per pass) and reads them back row-major, 16 lanes per token row
-// (8 for SwiGLU's 32 output features), so that every global load and store instruction covers
-// whole 128- or 256-byte row segments of 4 or 8 rows. The gated epilogues issue all their
-// residual and gate loads before the first store: loads and stores share one completion
-// counter, so a load issued after a store would be waited for together with that store.
-// Same values and roundings as the register epilogue: acc (fp32), then silu(g) u, or
-// resid + gate acc (fmaf), or the plain value, rounded once to the output type.
-template <int EPI>
-__device__ __forceinline__ void store_tile_staged(const GemmArgs& a, f32x16 (&acc)[2][4], int m0,
-                                                  int n0, int wm, int wn, int lane,
-                                                  lds_char_t* region) {
-  constexpr int TM = 128;                                  // tokens per wave
-  constexpr bool GATED = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_IN) ||
-                         (EPI == EPI_GATED_F32_TO_F32);
-  constexpr bool OUT_F32 = (EPI == EPI_GATED_TO_F32) || (EPI == EPI_GATED_F32_TO_F32);
-  constexpr bool RESID_F32 = (EPI == EPI_GATED_F32_IN) || (EPI == EPI_GATED_F32_TO_F32);
-  constexpr int OUT_T = (EPI == EPI_SWIGLU) ? 1 : 2;      // 32-feature output sub-tiles
-  constexpr int OF = OUT_T * 32;                           // output features of the wave
-  constexpr int LR = OF / 4;                               // lanes per token row
-  constexpr int RI = 64 / LR;                              // token rows per step
-  constexpr int TP = 128 / OF;                             // 32-row blocks per pass (16 KB)
-  constexpr int NP = 4 / TP;                               // passes
-  constexpr int RB = OF * 4;                               // bytes per staged row
-  constexpr int SPP = TP * 32 / RI;                        // steps per pass
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int rsub = lane / LR, q = lane % LR;
-  const int rows_total = total_rows(a.rows);
-  const int fb = n0 + wn * OF + 4 * q;                     // this lane's 4 output features
-  const int tok0 = m0 + wm * TM;
-  // A tile never straddles two requests: the request, its first row and its bounds are uniform.
-  int req = 0, base = 0, nvalid = a.rows.n_valid, nvideo = a.rows.n_video;
-  if (a.rows.batch > 1) {
-    req = m0 / a.rows.seq_pad;
-    base = req * a.rows.seq_pad;
-    nvalid = a.rows.req_valid[req];
-    nvideo = a.rows.req_video[req];
-  }
-  // Bank-conflict-free staging: 16-byte chunk c of row r sits at chunk c ^ sw(r), so that the 8
-  // (or 16) lanes that the LDS serves together, consecutive rows at one chunk when writing and
-  // the chunks of one or two rows when reading, fall on distinct 16-byte bank groups of 128 (or
-  // 256) bytes: sw = r mod 16 for 256-byte rows; for 128-byte rows sw = (r mod 8) ^ (r / 8 mod 2),
-  // a permutation on every 8 aligned rows that also separates the even (and the odd) rows of 16.
-  auto sw = [](int r) __attribute__((always_inline)) {
-    return RB == 256 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
-  };
-
-  if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[0][t][e] = silu_mul(acc[0][t][e], acc[1][t][e]);
-  }
-  auto stage = [&](int p) __attribute__((always_inline)) {
-#pragma unroll
-    for (int tt = 0; tt < TP; ++tt) {
-      const int row = tt * 32 + l32;
-#pragma unroll
-      for (int f = 0; f < OUT_T; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = 8 * f + 2 * j + hh;
-          const f32x4 v = {acc[f][p * TP + tt][4 * j], acc[f][p * TP + tt][4 * j + 1],
-                           acc[f][p * TP + tt][4 * j + 2], acc[f][p * TP + tt][4 * j + 3]};
-          *reinterpret_cast<lds_f32x4_t*>(region + row * RB + ((c ^ sw(row)) << 4)) = v;
-        }
-    }
-  };
-  __syncthreads();  // every wave is done with the ring's fragments
-  stage(0);
-
-  // gated: every residual the wave reads, then the gate terms (ada, temb) of both modalities
-  // for the lane's features, all in flight before the first store; the gate sum ada + temb is
-  // formed at its first use, so that no wait separates the loads
-  f32x4 rv[NP][SPP];
-  float4 ga[2], gt[2];
-  if constexpr (GATED) {
-    const int fc = fb < a.N ? fb : a.N - 4;
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int st = 0; st < SPP; ++st) {
-        int tok = tok0 + p * TP * 32 + st * RI + rsub;
-        tok = tok < rows_total ? tok : rows_total - 1;
-        if constexpr (RESID_F32) {
-          const float4 r4 = *reinterpret_cast<const float4*>(
-              static_cast<const float*>(a.resid) + (int64_t)tok * a.ldr + fc);
-          rv[p][st] = f32x4{r4.x, r4.y, r4.z, r4.w};
-        } else {
-          const u32x2 rr = *reinterpret_cast<const u32x2*>(
-              static_cast<const uint16_t*>(a.resid) + (int64_t)tok * a.ldr + fc);
-          rv[p][st] = f32x4{bf_lo(rr.x), bf_hi(rr.x), bf_lo(rr.y), bf_hi(rr.y)};
-        }
-      }
-#pragma unroll
-    for (int mod = 0; mod < 2; ++mod) {
-      const int64_t goff = ((int64_t)mod * 6 + a.chunk) * a.N + fc;
-      ga[mod] = *reinterpret_cast<const float4*>(a.ada + goff);
-      gt[mod] = *reinterpret_cast<const float4*>(a.temb + req * a.temb_stride + goff);
-    }
-  }
-
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    if (p > 0) stage(p);  // the wave's own reads of pass p - 1 precede these writes (LDS order)
-#pragma unroll
-    for (int st = 0; st < SPP; ++st) {
-      const int row = st * RI + rsub;
-      const f32x4 v = *reinterpret_cast<lds_f32x4_t*>(region + row * RB + ((q ^ sw(row)) << 4));
-      const int tok = tok0 + p * TP * 32 + row;
-      if (tok >= rows_total || fb >= a.N) continue;
-      const int i = tok - base;
-      float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (i < nvalid) {
-        if constexpr (GATED) {
-          const float4 g4 = i < nvideo ? make_float4(ga[0].x + gt[0].x, ga[0].y + gt[0].y,
-                                                     ga[0].z + gt[0].z, ga[0].w + gt[0].w)
-                                       : make_float4(ga[1].x + gt[1].x, ga[1].y + gt[1].y,
-                                                     ga[1].z + gt[1].z, ga[1].w + gt[1].w);
-          o[0] = fmaf(g4.x, v[0], rv[p][st][0]);
-          o[1] = fmaf(g4.y, v[1], rv[p][st][1]);
-          o[2] = fmaf(g4.z, v[2], rv[p][st][2]);
-          o[3] = fmaf(g4.w, v[3], rv[p][st][3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = v[e];
-        }
-      }
-      if constexpr (OUT_F32) {
-        float* crow = static_cast<float*>(a.C) + (int64_t)tok * a.ldc;
-        *reinterpret_cast<float4*>(crow + fb) = make_float4(o[0], o[1], o[2], o[3]);
-      } else {
-        uint16_t* crow = static_cast<uint16_t*>(a.C) + (int64_t)tok * a.ldc;
-        if (fb + 4 <= a.N) {
-          *reinterpret_cast<u32x2*>(crow + fb) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (fb + e < a.N) crow[fb + e] = to_bf16(o[e]);
-        }
-      }
-    }
-  }
-}
 
 template <int EPI>
 __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int tiles_n) {
@@ -656,7 +544,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
   }
   static_assert(FT == 2 && MT == 4 && TM == 128 && STAGES * kDlStageBytes == NW * 16384,
                 "staged epilogue: 128 x 64 accumulators and 16 KB of the ring per wave");
-  store_tile_staged<EPI>(a, acc, m0, n0, wm, wn, lane, (lds_char_t*)(lds_ring) + wave * 16384);
+  store_tile_staged<EPI, MT>(a, acc, m0, n0, wm, wn, lane, (lds_char_t*)(lds_ring) + wave * 16384);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, bool ALIGNED>
