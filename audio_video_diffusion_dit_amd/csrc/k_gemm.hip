@@ -8,7 +8,8 @@
 //  * WM x WN wave64s per workgroup; each wave owns a (BN/WN features) x (BM/WM tokens)
 //    accumulator block of 32x32 tiles of v_mfma_f32_32x32x16_bf16. The weight tile is the MFMA
 //    A operand and the token tile the B operand, so every lane ends up holding 4 consecutive
-//    output features of one token: epilogue loads/stores are 8- or 16-byte vectors.
+//    output features of one token; the epilogue turns that layout row-major through the LDS
+//    (see store_tile_staged) so that its loads and stores cover whole row segments.
 //  * k-tiles of 64 staged global -> registers -> LDS, double buffered, one barrier per k-tile.
 //    Global loads are raw buffer loads: rows past the valid range or past K read as zero from
 //    the hardware's range check, so the loop has no branches. The next tile's loads are issued
@@ -91,16 +92,17 @@ typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
 // Fused epilogue, staged through the LDS (free once every wave has passed the barrier at its
 // top). In the MFMA layout lane (l32, hh) holds features 32 f + 8 j + 4 hh .. + 3 of token
 // 32 t + l32 of its wave's block in acc[f][t][4 j .. 4 j + 3] (SwiGLU pairs gate sub-tile 0 with
-// up sub-tile 1), so a store instruction straight from the accumulators writes 8 or 16 bytes into
-// each of 32 token rows. Here each wave writes its 32 MT tokens x 64 features of fp32
-// accumulators into a private 16 KB region (64 tokens per pass) and reads them back row-major, 16
-// lanes per token row (8 for SwiGLU's 32 output features), so that every global load and store
-// instruction covers whole 128- or 256-byte row segments of 4 or 8 rows. Invalid rows (at or
-// past a request's valid length) are written 0, rows past the last request are not written. The gated epilogues issue all their
-// residual and gate loads before the first store: loads and stores share one completion
-// counter, so a load issued after a store would be waited for together with that store.
-// Same values and roundings as the register epilogue: acc (fp32), then silu(g) u, or
-// resid + gate acc (fmaf), or the plain value, rounded once to the output type.
+// up sub-tile 1), so a store instruction straight from the accumulators would write 8 or 16
+// bytes into each of 32 token rows. Instead each wave writes its 32 MT tokens x 64 features of
+// fp32 accumulators into a private 16 KB region of the LDS (as many tokens per pass as fit) and
+// reads them back row-major, 16 lanes per token row (8 for SwiGLU's 32 output features), so that
+// every global load and store instruction covers whole 128- or 256-byte row segments of 4 or 8
+// rows. The gated epilogues issue all their residual and gate loads before the first store:
+// loads and stores share one completion counter, so a load issued after a store would be
+// waited for together with that store. Values: acc (fp32), then silu(g) u, or
+// resid + gate acc (fmaf), or the plain value, rounded once to the output type. Invalid rows
+// (at or past a request's valid length) are written 0, rows past the last request are not
+// written.
 template <int EPI, int MT>
 __device__ __forceinline__ void store_tile_staged(const GemmArgs& a, f32x16 (&acc)[2][MT], int m0,
                                                   int n0, int wm, int wn, int lane,
