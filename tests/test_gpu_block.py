@@ -50,18 +50,21 @@ def _inter(dev, ws, m, wl):
 
 ODD = dict(name="block_odd", hidden=256, heads=2, head_dim=128, ffn=300, n_video=100,
            n_audio=37, seq_pad=200)
+# Large enough for the 256 x 256 direct-to-LDS tiles on the QKV and gate/up projections, with a
+# partial last feature tile in each (QKV: 3 x 1088 = 12.75 tiles of 256; SwiGLU: 2880 outputs =
+# 22.5 tiles of 128) and in the out- and down-projections on the 128 x 128 tiles (1088 = 8.5 x 128).
+TILES = dict(name="block_tiles", hidden=1088, heads=17, head_dim=64, ffn=2880, n_video=3000,
+             n_audio=1000, seq_pad=4096)
+EXTRA = {"block_odd": ODD, "block_tiles": TILES}
 
 
 def _case(name, seed=0):
     from audio_video_diffusion_dit_amd import inputs as I
-    if name == "block_odd":
-        wl = I.Workload(**ODD)
-    else:
-        wl = I.WORKLOADS[name]
+    wl = I.Workload(**EXTRA[name]) if name in EXTRA else I.WORKLOADS[name]
     return I.block_case(wl, seed=seed, n_blocks=1)
 
 
-@pytest.mark.parametrize("name", ["block_small", "block_odd"])
+@pytest.mark.parametrize("name", ["block_small", "block_odd", "block_tiles"])
 def test_block_end_to_end_and_per_kernel(env, name):
     import oracle as O
     N, dev = env
@@ -109,7 +112,7 @@ def test_block_end_to_end_and_per_kernel(env, name):
     assert_kernel_close(got[:V], x2_ref, "down GEMM + gated residual")
 
 
-@pytest.mark.parametrize("name", ["block_small", "block_odd"])
+@pytest.mark.parametrize("name", ["block_small", "block_odd", "block_tiles"])
 def test_block_modes_bitwise_and_deterministic(env, name):
     N, dev = env
     case = _case(name, seed=5)
