@@ -19,7 +19,8 @@ Pin status: every function is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute-force scalar loops, special cases or the cache counts the
 pages print, except ``block_forward`` as a whole, whose composition is pinned
 only through its parts and a brute-force scalar re-derivation on a tiny shape
-("parity unpinned" against the pages: they print no numeric example of a block), and
+("parity unpinned" against the pages: they print no numeric example of a block),
+``stack_forward``, pinned against those scalar loops chained by hand over two blocks, and
 ``velocity_head``, pinned by closed forms (one-hot rows, a scale of -1) and scalar loops.
 
 Diagnostics (never the graded reference): ``block_forward_bf16_storage`` and

@@ -430,6 +430,32 @@ def test_block_against_scalar_loops():
     assert np.allclose(sub, got[[0, 4, 6]], rtol=1e-13, atol=1e-14)
 
 
+def test_stack_against_chained_scalar_loops():
+    """The stack applies its blocks in the given order, each to the previous block's output
+    ([P1] section 1: the DiT runs its B blocks in sequence): two different blocks against the
+    scalar-loop block chained by hand, which a reversed order, an unchained input or a stack
+    that keeps only one block would all miss."""
+    D, H, Dh, F = 8, 2, 4, 6
+    n_v, n_a, L = 2, 2, 5
+    b1, temb = _tiny_block(21, D, H, Dh, F)
+    b2, _ = _tiny_block(22, D, H, Dh, F)
+    rng = np.random.default_rng(23)
+    x = np.zeros((L, D))
+    x[: n_v + n_a] = rng.standard_normal((n_v + n_a, D))
+    dims = O.Dims(D, H, Dh, F, rope_base=100.0)
+    lay = O.Layout(n_v, n_a, L)
+    got = O.stack_forward(x, [b1, b2], temb, dims, lay)
+    count = [0]
+    mid = _block_brute(x, b1, temb, D, H, Dh, F, n_v, n_a, L, 1e-6, 1e-6, 100.0, count)
+    want = _block_brute(mid, b2, temb, D, H, Dh, F, n_v, n_a, L, 1e-6, 1e-6, 100.0, count)
+    assert np.allclose(got, want, rtol=1e-10, atol=1e-12)
+    other = _block_brute(_block_brute(x, b2, temb, D, H, Dh, F, n_v, n_a, L, 1e-6, 1e-6, 100.0,
+                                      count), b1, temb, D, H, Dh, F, n_v, n_a, L, 1e-6, 1e-6,
+                         100.0, count)
+    assert not np.allclose(got, other, rtol=1e-6), "the two blocks must not commute here"
+    assert np.array_equal(O.stack_forward(x, [], temb, dims, lay), x)
+
+
 def test_bf16_scalar_rounding_reference():
     # the bracketing rounding used by the scalar loops agrees with hand-derived cases
     assert _bf16_scalar(1.0) == 1.0
