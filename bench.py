@@ -63,7 +63,7 @@ def parse():
     p.add_argument("--only", default=None,
                    help="with --configs: comma-separated subset of block_small, loop_4blk, "
                         "block_h3, loop_8blk_32k, loop_4blk_loop, block_ragged, head_32k, "
-                        "attn_ragged, attn_ragged_qknorm")
+                        "attn_ragged, attn_ragged_qknorm, rank_share")
     return p.parse_args()
 
 
@@ -416,6 +416,66 @@ def configs_report(args):
                              "sample": f"{rows_per} query rows per request, all heads and keys"}
         emit(rec)
 
+    def rank_share():
+        """One rank's share of a P-way Ulysses split of the 32768-token block (the split itself
+        is not built; one GPU measures one rank's kernels): attention over all 32768 tokens with
+        24 / P heads, q and k through the Q/K RMSNorm with gains as in the block, and the rest of
+        the block on 32768 / P rows, timed as the block at that length minus its own attention.
+        The two all-to-alls around attention are not measured."""
+        log("[configs] rank_share")
+        wl = I.WORKLOADS["loop_8blk_32k"]
+        D, H, Dh, F, L = wl.hidden, wl.heads, wl.head_dim, wl.ffn, wl.seq_pad
+        rng = np.random.Generator(np.random.PCG64(12))
+        blk = dev.upload_block(I.make_block(rng, wl))
+        gq = dev.to_dev_f32(np.ones(Dh, np.float32))
+        gen = torch.Generator(device="cuda").manual_seed(12)
+
+        def unit_heads(n_rows, heads):
+            t = torch.randn((n_rows, heads, Dh), device="cuda", generator=gen)
+            return (t / torch.sqrt((t * t).mean(-1, keepdim=True) + 1e-6)).to(torch.bfloat16)
+
+        res = []
+        t_one = None
+        for P in (1, 2, 4, 8):
+            h = H // P
+            q, k, v = unit_heads(L, h), unit_heads(L, h), unit_heads(L, h)
+            o = torch.empty_like(q)
+            attn_ms = gpu_ms(lambda: N.dit_attention_forward(
+                q, k, v, o, 1, L, h, Dh, L * h * Dh, h * Dh, L * h * Dh, h * Dh, [L],
+                N.DIT_ATTN_VALID_ONLY, stream=stream, q_gain=gq, k_gain=gq))
+            del q, k, v, o
+            Vp = L // P
+            nv = Vp * wl.n_video // L
+            wlp = I.Workload(f"rank_{P}", D, H, Dh, F, nv, Vp - nv, Vp)
+            dims, lay = dev.dims_of(wlp), dev.layout_of(wlp)
+            x = dev.to_dev_bf16(I.bf16_bits(rng.standard_normal((Vp, D), dtype=np.float32)))
+            temb = dev.to_dev_f32(rng.standard_normal((2, 6, D), dtype=np.float32))
+            out = torch.empty_like(x)
+            ws, m = dev.workspace(dims, lay, 0)
+            block_ms = gpu_ms(lambda: N.dit_block_forward(dims, lay, blk.weights, temb, x, out,
+                                                          N.DIT_ATTN_VALID_ONLY, ws,
+                                                          stream=stream))
+            qkv = ws.data_ptr() + m.qkv
+            att = ws.data_ptr() + m.attn_out
+            local_ms = gpu_ms(lambda: N.dit_attention_forward(
+                qkv, qkv + 2 * D, qkv + 4 * D, att, 1, Vp, H, Dh, Vp * 3 * D, 3 * D, Vp * D, D,
+                [Vp], N.DIT_ATTN_VALID_ONLY, stream=stream, q_gain=blk.weights.q_g,
+                k_gain=blk.weights.k_g))
+            del x, out, ws
+            rest_ms = block_ms - local_ms
+            rank_ms = attn_ms + rest_ms
+            if P == 1:
+                t_one = rank_ms
+            res.append({"P": P, "heads_per_rank": h, "rows_per_rank": Vp,
+                        "attention_workgroups": (L + 255) // 256 * h,
+                        "attention_ms": round(attn_ms, 4),
+                        "attention_tflops": round(4.0 * L * L * h * Dh / attn_ms / 1e9, 1),
+                        "rest_of_block_ms": round(rest_ms, 4),
+                        "rank_block_ms": round(rank_ms, 4),
+                        "compute_efficiency_vs_one_gpu": round(t_one / (P * rank_ms), 4)})
+        emit({"workload": "rank_share", "kind": "per-rank kernels of a Ulysses split",
+              "hidden": D, "heads": H, "head_dim": Dh, "ffn": F, "seq": L, "shares": res})
+
     for name, rows_n in (("block_small", None), ("loop_4blk", None), ("block_h3", 256),
                          ("loop_8blk_32k", 256)):
         if want(name):
@@ -430,6 +490,8 @@ def configs_report(args):
         attn_ragged(False)
     if want("attn_ragged_qknorm"):
         attn_ragged(True)
+    if want("rank_share"):
+        rank_share()
 
 
 def hbm_reference(args):
