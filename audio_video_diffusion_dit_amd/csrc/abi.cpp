@@ -739,6 +739,7 @@ int head_impl(const dit_dims* dims, const dit_layout* layout, const dit_head_wei
   if ((st = check_aligned16(temb, "temb")) != DIT_OK) return st;
   if ((st = check_aligned16(hw->norm_g, "norm_g")) != DIT_OK) return st;
   if ((st = check_aligned16(hw->ada, "ada")) != DIT_OK) return st;
+  if ((st = check_aligned16(hw->w_out, "w_out")) != DIT_OK) return st;
   const size_t need = head_ws_bytes(dims, C);
   if ((st = check_ws(ws, ws_bytes, need)) != DIT_OK) return st;
   const int32_t D = dims->hidden, L = layout->seq_pad;

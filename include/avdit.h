@@ -21,10 +21,10 @@
  *    except a thread-local error string. Device work is enqueued asynchronously on the
  *    given stream (NULL = the default stream); calls return after enqueueing.
  *  - Alignment: activations (x_in, x_out, latents, velocities), temb tables, and the fp32
- *    parameters norm1_g, norm2_g, q_g, k_g, ada (and the head's norm_g, ada, bias) are read
- *    or written with 16-byte vector accesses and must be 16-byte aligned (DIT_ERR_INVALID
- *    otherwise). bf16 weight matrices may have any 2-byte alignment; unaligned ones take a
- *    slower loader.
+ *    parameters norm1_g, norm2_g, q_g, k_g, ada (and the head's norm_g, ada, bias and its
+ *    bf16 w_out) are read or written with 16-byte vector accesses and must be 16-byte aligned
+ *    (DIT_ERR_INVALID otherwise). The block's bf16 weight matrices may have any 2-byte
+ *    alignment; unaligned ones take a slower loader.
  *  - Size limits: the kernels address their large operands through 32-bit byte offsets,
  *    so each of these must span less than 2 GiB, else DIT_ERR_UNSUPPORTED: the weights
  *    w_qkv, w_gate_up, w_down; the block activations [rows, D] and the SwiGLU activations
@@ -140,7 +140,7 @@ typedef struct {
  * AdaLN layer with a table of its own; [P1] section 1: the DiT predicts the flow-matching
  * velocity).
  *   norm_g [D]; ada [n_mod, 2, D], rows shift then scale;
- *   w_out bf16 [n_mod, out_channels, D]: one [out, in] matrix per modality;
+ *   w_out bf16 [n_mod, out_channels, D], 16-byte aligned: one [out, in] matrix per modality;
  *   bias fp32 [n_mod, out_channels], 16-byte aligned, or NULL for none;
  *   out_channels: a positive multiple of 8, at most 65536. */
 typedef struct {

@@ -353,11 +353,12 @@ def test_vector_accessed_pointers_must_be_aligned(N):
     code = N.lib.denoise_loop(d, lay, (N.DitBlockWeights * 1)(N.DitBlockWeights(*good)), 1, 1, sig,
                               sig, 256 + 8, N.make_policy("off"), 1 << 20, 0, None, big, need_l, None)
     assert code == N.DIT_ERR_INVALID
-    # the head's norm gain, table and temb
+    # the head's norm gain, table, output weights and temb
     need_h = N.dit_head_workspace_size(d, lay, 64)
     g = N.lib.dit_velocity_head
     for head in (N.DitHeadWeights(256 + 4, 512, 1 << 24, 1 << 25, 64),
-                 N.DitHeadWeights(256, 512 + 8, 1 << 24, 1 << 25, 64)):
+                 N.DitHeadWeights(256, 512 + 8, 1 << 24, 1 << 25, 64),
+                 N.DitHeadWeights(256, 512, (1 << 24) + 8, 1 << 25, 64)):
         assert g(d, lay, head, 1 << 20, 1 << 32, 1 << 34, 1 << 30, need_h, None) == N.DIT_ERR_INVALID
     head = N.DitHeadWeights(256, 512, 1 << 24, 1 << 25, 64)
     assert g(d, lay, head, (1 << 20) + 4, 1 << 32, 1 << 34, 1 << 30, need_h, None) == N.DIT_ERR_INVALID
