@@ -69,16 +69,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // Tile selection: workgroup ids are dealt round-robin over the 8 XCDs; each XCD receives a
-// contiguous range of tiles, ordered in groups of 6 token-tiles, so that the workgroups resident
-// on one XCD share operand panels in its L2. (Measured on the 32k block's projections: groups of
-// 3 to 6 beat 8 by 3-5% over the four GEMMs, 16 is 10% slower.)
-__device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_m, int& tile_n) {
+// contiguous range of tiles, ordered in groups of GM token-tiles, so that the workgroups resident
+// on one XCD share operand panels in its L2. GM is 6, or 3 for a long reduction (K >= 2 N: the
+// down projection), chosen by the launcher from kernel-trace sweeps of GM = 2, 3, 4, 6 (8 and 16
+// were slower) on the 32k-token and 13,440-token blocks: the down projection ran 3-5% faster
+// with 3, the other three projections fastest with 6 or within 1% of it.
+__device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_m, int& tile_n,
+                                            int GM = 6) {
   const int nt = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int per = nt >> 3, rem = nt & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
-  constexpr int GM = 6;
   const int group = logical / (GM * tiles_n);
   const int first_m = group * GM;
   const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
@@ -427,7 +429,7 @@ __device__ __forceinline__ void dl_b128(uint32_t lds_base, uint32_t voffset, i32
 __device__ __forceinline__ int dl_swz(int r) { return (r >> 1) & 7; }
 
 template <int EPI>
-__global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int tiles_n, int gm) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
   constexpr int STAGES = kDlStages;
   constexpr int NW = WM * WN;
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
   int tile_m, tile_n;
-  select_tile(tiles_m, tiles_n, tile_m, tile_n);
+  select_tile(tiles_m, tiles_n, tile_m, tile_n, gm);
   const int m0 = tile_m * BM;
   const int rows_total = total_rows(a.rows);
   const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
@@ -625,12 +627,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int tiles_m = (total_rows(a.rows) + 255) / 256;
     const int tiles_n = (a.N + out_big - 1) / out_big;
     const dim3 grid(tiles_m * tiles_n), block(512);
+    const int gm = (a.K >= 2 * a.N) ? 3 : 6;  // token-tiles per group (see select_tile)
     switch (a.epilogue) {
-      case EPI_STORE: hipLaunchKernelGGL(k_gemm_dl<EPI_STORE>, grid, block, 0, s, a, tiles_m, tiles_n); break;
-      case EPI_GATED_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
-      case EPI_GATED_F32_IN: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_IN>, grid, block, 0, s, a, tiles_m, tiles_n); break;
-      case EPI_GATED_F32_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_dl<EPI_SWIGLU>, grid, block, 0, s, a, tiles_m, tiles_n); break;
+      case EPI_STORE: hipLaunchKernelGGL(k_gemm_dl<EPI_STORE>, grid, block, 0, s, a, tiles_m, tiles_n, gm); break;
+      case EPI_GATED_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n, gm); break;
+      case EPI_GATED_F32_IN: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_IN>, grid, block, 0, s, a, tiles_m, tiles_n, gm); break;
+      case EPI_GATED_F32_TO_F32: hipLaunchKernelGGL(k_gemm_dl<EPI_GATED_F32_TO_F32>, grid, block, 0, s, a, tiles_m, tiles_n, gm); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_dl<EPI_SWIGLU>, grid, block, 0, s, a, tiles_m, tiles_n, gm); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
