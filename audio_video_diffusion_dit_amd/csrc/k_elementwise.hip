@@ -13,13 +13,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------------------
 // RMSNorm fused with indexed AdaLN modulation (TeleFuser PR #38, section 2; TeleFuser PR #23,
 // "Changes Made": indexed modulation). The input is the bf16 block input (norm1) or the fp32
-// mid-block residual (norm2). One wave owns a run of 8 consecutive rows and keeps the next
-// row's loads (fp32 rows: the next two rows') in flight while it reduces the current one; the modulation of the current
-// modality, folded to mul = g * (1 + scale) and add = shift, stays in registers and is
-// reloaded only when the run crosses the video/audio boundary, so the tables cost almost no
-// cache traffic per row.
+// mid-block residual (norm2). One wave owns a run of up to 8 consecutive rows and keeps the
+// next row's loads (fp32 rows: the next two rows') in flight while it reduces the current one;
+// the modulation of the current modality, folded to mul = g * (1 + scale) and add = shift,
+// stays in registers and is reloaded only when the run crosses the video/audio boundary, so the
+// tables cost little cache traffic per row. Shorter runs at short sequences keep enough waves in
+// flight (a wave's rows are a chain of memory round trips).
 // ---------------------------------------------------------------------------------------
+// Rows per wave: 8, or fewer when 8 would leave under kNormWaves waves. Measured on the
+// hidden-1024 block (4,608 rows): 3 rows per wave 9.0 us against 13.5 us for 8 (norm1); on
+// the hidden-3072 block of 13,568 rows, 7 rows per wave was 1-4% faster than 8 and 4 rows
+// 12-19% slower (every wave first loads its modulation rows, 60 KB at hidden 3072).
 constexpr int kNormRowsPerWave = 8;
+constexpr int kNormWaves = 2048;
 
 // Row data as loaded: 8 elements per chunk, bf16 (one 16-byte word) or fp32 (two).
 template <bool F32IN>
@@ -66,7 +72,7 @@ __device__ __forceinline__ void unpack_chunk(const RowChunk<F32IN>& r, float (&x
 }
 
 template <int CPL, bool F32IN>  // CPL: 8-element chunks per lane, ceil(D / 512)
-__global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
+__global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a, int rpw) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (readfirstlane): the per-request lookups of a batch then become scalar loads,
   // whose wait does not drain the rows prefetched with vector loads
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
   float add[CPL][8];
   int cur = -1;   // (request, modality) whose modulation the registers hold
   const int rows_total = total_rows(a.rows);
-  const int row0 = wave * kNormRowsPerWave;
+  const int row0 = wave * rpw;
   if (row0 >= rows_total) return;
 
   // software pipeline: the next row's loads are in flight while the current row is reduced
@@ -90,11 +96,11 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
     if (row0 + 1 < rows_total && row_info(a.rows, row0 + 1).valid)
       load_row<CPL, F32IN>(a, row0 + 1, lane, nchunk, nxt);
   }
-  for (int rr = 0; rr < kNormRowsPerWave; ++rr) {
+  for (int rr = 0; rr < rpw; ++rr) {
     const int row = row0 + rr;
     if (row >= rows_total) return;
     const RowInfo ri = row_info(a.rows, row);
-    if (rr + AHEAD < kNormRowsPerWave && row + AHEAD < rows_total &&
+    if (rr + AHEAD < rpw && row + AHEAD < rows_total &&
         row_info(a.rows, row + AHEAD).valid)
       load_row<CPL, F32IN>(a, row + AHEAD, lane, nchunk, AHEAD == 2 ? nx2 : nxt);
     uint4* out = reinterpret_cast<uint4*>(a.h + (size_t)row * D);
@@ -171,13 +177,17 @@ __global__ __launch_bounds__(256) void k_norm_mod(NormModArgs a) {
 
 template <int CPL>
 static hipError_t norm_mod_instance(const NormModArgs& a, hipStream_t s) {
-  const int waves = (total_rows(a.rows) + kNormRowsPerWave - 1) / kNormRowsPerWave;
+  const int rows = total_rows(a.rows);
+  // rows per wave: up to 8, fewer when that leaves under kNormWaves waves
+  int rpw = (rows + kNormWaves - 1) / kNormWaves;
+  rpw = rpw < 1 ? 1 : (rpw > kNormRowsPerWave ? kNormRowsPerWave : rpw);
+  const int waves = (rows + rpw - 1) / rpw;
   const int blocks = (waves + 3) / 4;
   if (blocks == 0) return hipSuccess;
   if (a.x_f32)
-    hipLaunchKernelGGL((k_norm_mod<CPL, true>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_norm_mod<CPL, true>), dim3(blocks), dim3(256), 0, s, a, rpw);
   else
-    hipLaunchKernelGGL((k_norm_mod<CPL, false>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_norm_mod<CPL, false>), dim3(blocks), dim3(256), 0, s, a, rpw);
   return hipGetLastError();
 }
 
@@ -199,7 +209,9 @@ hipError_t launch_norm_mod(const NormModArgs& a, hipStream_t s) {
 // PR #23, "Changes Made"). A group of head_dim/8 lanes owns one token: lane j holds
 // elements 8j..8j+7 of a head vector, so the rotate-half partner of lane j is lane
 // j ^ (group/2). The token's rotation angles are computed once (one sincos per element
-// slot) and reused for all 2H vectors (q heads then k heads, contiguous in qkv).
+// slot) and reused for all 2H vectors (q heads then k heads, contiguous in qkv); at short
+// sequences the vectors of a token are split over gridDim.y lane groups (each computing the
+// angles again) so that enough waves are in flight.
 // ---------------------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
@@ -241,12 +253,17 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
   const int nvec = 2 * a.heads;
 
   constexpr int U = 8;
-  for (int v0 = 0; v0 < nvec; v0 += U) {
+  // this lane group's vectors: a contiguous share of whole U-vector chunks
+  const int chunks = (nvec + U - 1) / U;
+  const int per = (chunks + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int v_begin = (int)blockIdx.y * per * U;
+  const int v_end = v_begin + per * U < nvec ? v_begin + per * U : nvec;
+  for (int v0 = v_begin; v0 < v_end; v0 += U) {
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      raw[u] = (v0 + u < nvec) ? *reinterpret_cast<const uint4*>(base + (size_t)(v0 + u) * DH)
-                               : zero4();
+      raw[u] = (v0 + u < v_end) ? *reinterpret_cast<const uint4*>(base + (size_t)(v0 + u) * DH)
+                                : zero4();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int vec = v0 + u;
@@ -276,26 +293,35 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkNormRopeArgs a) {
                                     : fmaf(y[e + 1], cs[e + 1], p1 * sn[e + 1]);
         o[e / 2] = pack_bf16x2(r0, r1);
       }
-      if (vec < nvec)
+      if (vec < v_end)
         *reinterpret_cast<uint4*>(base + (size_t)vec * DH) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
+
+// Lane groups per token: enough to reach kQkWaves waves, at most one per 8-vector chunk
+// (measured: 15.2 -> 13.0 us at 4,608 tokens x 16 vectors, 64.5 -> 57.2 us at 13,440 x 48;
+// the 32k-token launch already has 8192 waves and keeps one group per token).
+constexpr int kQkWaves = 8192;
 
 hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t s) {
   if ((a.row_stride & 7) != 0) return hipErrorInvalidValue;
   // one request: the valid rows; a batch: every row (invalid ones return at once)
   const int n = a.rows.batch > 1 ? total_rows(a.rows) : a.rows.n_valid;
   if (n <= 0) return hipSuccess;
-  if (a.head_dim == 128) {
-    const int tpb = 256 / 16;
-    hipLaunchKernelGGL(k_qk_norm_rope<128>, dim3((n + tpb - 1) / tpb), dim3(256), 0, s, a);
-  } else if (a.head_dim == 64) {
-    const int tpb = 256 / 8;
-    hipLaunchKernelGGL(k_qk_norm_rope<64>, dim3((n + tpb - 1) / tpb), dim3(256), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (a.head_dim != 128 && a.head_dim != 64) return hipErrorInvalidValue;
+  const int tpb = 256 / (a.head_dim / 8);  // tokens per block
+  const int blocks = (n + tpb - 1) / tpb;
+  // split a token's 8-vector chunks over more lane groups while the grid has fewer than
+  // kQkWaves waves
+  const int chunks = (2 * a.heads + 7) / 8;
+  int split = (kQkWaves + 4 * blocks - 1) / (4 * blocks);
+  split = split < 1 ? 1 : (split > chunks ? chunks : split);
+  const dim3 grid(blocks, split);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(k_qk_norm_rope<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_qk_norm_rope<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
