@@ -55,7 +55,12 @@ ODD = dict(name="block_odd", hidden=256, heads=2, head_dim=128, ffn=300, n_video
 # 22.5 tiles of 128) and in the out- and down-projections on the 128 x 128 tiles (1088 = 8.5 x 128).
 TILES = dict(name="block_tiles", hidden=1088, heads=17, head_dim=64, ffn=2880, n_video=3000,
              n_audio=1000, seq_pad=4096)
-EXTRA = {"block_odd": ODD, "block_tiles": TILES}
+# A reduction that is not a multiple of 64 (FFN 2856) over enough rows that the down projection
+# runs the 128 x 128 register-staged tiles in more than one round (59 x 9 = 531 tiles for 512
+# slots); the other projections take the 256 x 256 direct-to-LDS tiles.
+KPAD = dict(name="block_kpad", hidden=1088, heads=17, head_dim=64, ffn=2856, n_video=6000,
+            n_audio=1500, seq_pad=8192)
+EXTRA = {"block_odd": ODD, "block_tiles": TILES, "block_kpad": KPAD}
 
 
 def _case(name, seed=0):
@@ -169,6 +174,58 @@ def test_block_h3_sampled_rows(env):
     rows = np.sort(np.concatenate([rng.choice(V, 44, replace=False), [0, wl.n_video - 1, wl.n_video, V - 1]]))
     check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl, "block_h3 sampled rows",
                 rows=rows)
+
+
+def test_block_kpad_sampled_rows(env):
+    """Hidden 1088, FFN 2856 (not a multiple of 64), 7500 valid of 8192 rows: 48 sampled output
+    rows against the oracle, which computes keys and values for every valid row."""
+    N, dev = env
+    case = _case("block_kpad")
+    wl = case.wl
+    V = wl.n_valid
+    say(f"block_kpad sampled rows: V={V} L={wl.seq_pad} F={wl.ffn}")
+    out, _, _ = _gpu_block(env, case)
+    got = dev.bf16_values_of(out).astype(np.float64)
+    assert np.all(got[V:] == 0)
+    rng = np.random.default_rng(12)
+    rows = np.sort(np.concatenate([rng.choice(V, 44, replace=False), [0, wl.n_video - 1, wl.n_video, V - 1]]))
+    check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl, "block_kpad sampled rows",
+                rows=rows)
+
+
+@pytest.mark.parametrize("name", ["block_small", "block_odd"])
+def test_block_unaligned_gemm_weights_bitwise(env, name):
+    """Projection weights that start 2 bytes past a 16-byte boundary take the GEMMs' element-wise
+    operand path (128 x 128 tiles instead of the aligned 64 x 128 ones). The block output equals
+    the aligned call's bit for bit: every output sums the same products in the same order."""
+    import torch
+    N, dev = env
+    case = _case(name, seed=5)
+    wl = case.wl
+    out_a, _, _ = _gpu_block(env, case)
+    bp = case.blocks[0]
+
+    def off_by_one(bits):  # bf16 bits placed one element past a 16-byte-aligned start
+        flat = np.concatenate([np.zeros(1, np.uint16), np.ascontiguousarray(bits).reshape(-1)])
+        t = dev.to_dev_bf16(flat)
+        assert t.data_ptr() % 16 == 0
+        return t[1:]
+
+    t = dict(w_qkv=off_by_one(bp.w_qkv), w_o=off_by_one(bp.w_o), w_gate_up=off_by_one(bp.w_gate_up),
+             w_down=off_by_one(bp.w_down), norm1_g=dev.to_dev_f32(bp.norm1_g),
+             norm2_g=dev.to_dev_f32(bp.norm2_g), q_g=dev.to_dev_f32(bp.q_g), k_g=dev.to_dev_f32(bp.k_g),
+             ada=dev.to_dev_f32(bp.ada))
+    assert all(t[k].data_ptr() % 16 == 2 for k in ("w_qkv", "w_o", "w_gate_up", "w_down"))
+    dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+    x = dev.to_dev_bf16(case.x)
+    out_u = torch.empty_like(x)
+    out_u.view(torch.int16).fill_(0x7FC0)
+    ws, m = dev.workspace(dims, lay, 0)
+    N.dit_block_forward(dims, lay, N.make_block_weights(t), dev.to_dev_f32(case.temb), x, out_u, 0, ws)
+    torch.cuda.synchronize()
+    a, u = dev.bf16_bits_of(out_a), dev.bf16_bits_of(out_u)
+    say(f"block {name}: unaligned weights, {np.count_nonzero(a != u)} of {a.size} output values differ")
+    assert np.array_equal(a, u)
 
 
 @pytest.mark.parametrize("name,gain,path", [("block_small", 1.2, "shift-free"),
