@@ -22,8 +22,9 @@
 //    which keeps both the 16-byte fragment reads (32 rows, same chunk) and the loader's writes
 //    free of bank conflicts.
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin over the 8 XCDs)
-//    receives a contiguous range of tiles, and tiles are ordered in groups of 6 token-tiles,
-//    so the workgroups resident on one XCD share operand panels in that XCD's L2.
+//    receives a contiguous range of tiles, ordered in groups of token-tiles, so the workgroups
+//    resident on one XCD share operand panels in that XCD's L2; the tiles that hold valid rows
+//    are shared evenly over the XCDs before the tail tiles (see select_tile).
 //  * Rows at or beyond n_valid are never multiplied: their loads read zero and a tile that lies
 //    entirely in the tail only writes zeros (the zero-tail merge of TeleFuser PR #38, section 2).
 #include "common.hpp"
@@ -69,25 +70,75 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-// Tile selection: workgroup ids are dealt round-robin over the 8 XCDs; each XCD receives a
-// contiguous range of tiles, ordered in groups of GM token-tiles, so that the workgroups resident
-// on one XCD share operand panels in its L2. GM is 6, or 3 for a long reduction (K >= 2 N: the
-// down projection), chosen by the launcher from kernel-trace sweeps of GM = 2, 3, 4, 6 (8 and 16
-// were slower) on the 32k-token and 13,440-token blocks: the down projection ran 3-5% faster
-// with 3, the other three projections fastest with 6 or within 1% of it.
-__device__ __forceinline__ void select_tile(int tiles_m, int tiles_n, int& tile_m, int& tile_n,
-                                            int GM = 6) {
+// Token-tiles of bm rows that hold a valid row ("work" tiles) and those wholly in a tail (which
+// only write zeros), counted over the requests of a batch (bm divides a request's rows).
+__device__ __forceinline__ int work_mtiles(const RowLayout& r, int bm, int tiles_m) {
+  if (r.batch <= 1) {
+    const int v = (r.n_valid + bm - 1) / bm;
+    return v < tiles_m ? v : tiles_m;
+  }
+  const int tpr = r.seq_pad / bm;
+  int n = 0;
+  for (int b = 0; b < r.batch; ++b) {
+    const int v = (r.req_valid[b] + bm - 1) / bm;
+    n += v < tpr ? v : tpr;
+  }
+  return n;
+}
+// Index of the j-th work token-tile (work) or the j-th tail token-tile (!work), in row order.
+__device__ __forceinline__ int nth_mtile(const RowLayout& r, int bm, int tiles_m, int j, bool work) {
+  if (r.batch <= 1) {
+    const int v = work_mtiles(r, bm, tiles_m);
+    return work ? j : v + j;
+  }
+  const int tpr = r.seq_pad / bm;
+  for (int b = 0; b < r.batch; ++b) {
+    int v = (r.req_valid[b] + bm - 1) / bm;
+    v = v < tpr ? v : tpr;
+    const int c = work ? v : tpr - v;
+    if (j < c) return b * tpr + (work ? j : v + j);
+    j -= c;
+  }
+  return tiles_m - 1;  // not reached: j is below the count of its kind
+}
+
+// Tile selection: workgroup ids are dealt round-robin over the 8 XCDs, so XCD x runs the ids
+// b = x (mod 8), in order. Each XCD receives an equal contiguous share of the work tiles first,
+// then an equal share of the tail tiles, so that a ragged batch (whose short requests leave
+// whole token-tiles in their tails) loads the XCDs evenly; with the tail tiles ordered after
+// the work tiles an XCD holding short requests would otherwise finish long before one holding
+// full ones. Work tiles are ordered in groups of GM token-tiles, so that the workgroups
+// resident on one XCD share operand panels in its L2. GM is 6, or 3 for a long reduction
+// (K >= 2 N: the down projection), chosen by the launcher from kernel-trace sweeps of
+// GM = 2, 3, 4, 6 (8 and 16 were slower) on the 32k-token and 13,440-token blocks: the down
+// projection ran 3-5% faster with 3, the other three projections fastest with 6 or within 1%
+// of it. The map from ids to tiles is a bijection for any counts (each XCD's share of work
+// tiles never exceeds its share of ids).
+__device__ __forceinline__ void select_tile(const RowLayout& rows, int bm, int tiles_m,
+                                            int tiles_n, int& tile_m, int& tile_n, int GM = 6) {
   const int nt = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
-  const int per = nt >> 3, rem = nt & 7;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
-  const int group = logical / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-  const int in_group = logical - group * GM * tiles_n;
-  tile_m = first_m + in_group % gm;
-  tile_n = in_group / gm;
+  const int mw = work_mtiles(rows, bm, tiles_m);
+  const int wt = mw * tiles_n;
+  const int per_t = nt >> 3, rem_t = nt & 7;
+  const int per_w = wt >> 3, rem_w = wt & 7;
+  const int base_w = xcd * per_w + (xcd < rem_w ? xcd : rem_w);
+  const int w_x = per_w + (xcd < rem_w ? 1 : 0);
+  if (local < w_x) {
+    const int logical = base_w + local;
+    const int group = logical / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = (mw - first_m) < GM ? (mw - first_m) : GM;
+    const int in_group = logical - group * GM * tiles_n;
+    tile_m = nth_mtile(rows, bm, tiles_m, first_m + in_group % gm, true);
+    tile_n = in_group / gm;
+  } else {
+    const int base_t = xcd * per_t + (xcd < rem_t ? xcd : rem_t);
+    const int z = base_t - base_w + (local - w_x);
+    tile_m = nth_mtile(rows, bm, tiles_m, z / tiles_n, false);
+    tile_n = z % tiles_n;
+  }
 }
 
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
@@ -277,7 +328,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm(GemmArgs a, int tiles_
   const int wn = wave / WM;   // feature slice
 
   int tile_m, tile_n;
-  select_tile(tiles_m, tiles_n, tile_m, tile_n);
+  select_tile(a.rows, BM, tiles_m, tiles_n, tile_m, tile_n);
 
   const int m0 = tile_m * BM;
   const int rows_total = total_rows(a.rows);
@@ -454,7 +505,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_dl(GemmArgs a, int tiles_m, int
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
   int tile_m, tile_n;
-  select_tile(tiles_m, tiles_n, tile_m, tile_n, gm);
+  select_tile(a.rows, BM, tiles_m, tiles_n, tile_m, tile_n, gm);
   const int m0 = tile_m * BM;
   const int rows_total = total_rows(a.rows);
   const int n0 = (EPI == EPI_SWIGLU) ? tile_n * (BN / 2) : tile_n * BN;
