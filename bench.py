@@ -63,7 +63,7 @@ def parse():
     p.add_argument("--only", default=None,
                    help="with --configs: comma-separated subset of block_small, loop_4blk, "
                         "block_h3, loop_8blk_32k, loop_4blk_loop, block_ragged, head_32k, "
-                        "attn_ragged, attn_ragged_qknorm, rank_share")
+                        "attn_ragged, attn_ragged_qknorm, rank_share, variants")
     return p.parse_args()
 
 
@@ -476,6 +476,67 @@ def configs_report(args):
         emit({"workload": "rank_share", "kind": "per-rank kernels of a Ulysses split",
               "hidden": D, "heads": H, "head_dim": Dh, "ffn": F, "seq": L, "shares": res})
 
+    def variants():
+        """The fp32 residual-stream block beside the bf16 one (same box, same inputs), and the
+        4-block loop with the fp32 residual stream and with the extrapolating cache mode, each
+        compared with the bf16 cache-off loop's final latents (report only)."""
+        log("[configs] variants")
+        blocks_rec = []
+        for name in ("block_h3", "loop_8blk_32k"):
+            wl = I.WORKLOADS[name]
+            case = I.block_case(wl, seed=0, n_blocks=1)
+            dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+            blk = dev.upload_block(case.blocks[0])
+            temb = dev.to_dev_f32(case.temb)
+            xb = dev.to_dev_bf16(case.x)
+            xf = dev.to_dev_f32(I.bf16_to_f32(case.x))
+            ob, of = torch.empty_like(xb), torch.empty_like(xf)
+            ws, _ = dev.workspace(dims, lay, 0)
+            ms_b = gpu_ms(lambda: N.dit_block_forward(dims, lay, blk.weights, temb, xb, ob,
+                                                      N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
+            ms_f = gpu_ms(lambda: N.dit_block_forward_f32(dims, lay, blk.weights, temb, xf, of,
+                                                          N.DIT_ATTN_VALID_ONLY, ws, stream=stream))
+            fl = block_flops(wl.n_valid, wl.hidden, wl.ffn)
+            blocks_rec.append({"workload": name, "valid": wl.n_valid, "seq_pad": wl.seq_pad,
+                               "bf16_residual_ms": round(ms_b, 4), "fp32_residual_ms": round(ms_f, 4),
+                               "fp32_residual_tflops": round(fl / ms_f / 1e9, 2),
+                               "fp32_over_bf16": round(ms_f / ms_b, 4)})
+            del ws, blk, xb, xf, ob, of
+        wl = I.WORKLOADS["loop_4blk"]
+        case = I.loop_case(wl, seed=0)
+        dims, lay = dev.dims_of(wl), dev.layout_of(wl)
+        blocks = dev.upload_blocks(case.blocks)
+        bw = [b.weights for b in blocks]
+        temb = dev.to_dev_f32(case.temb_steps)
+        x0 = dev.to_dev_f32(case.x0)
+        x = torch.empty_like(x0)
+        ws, _ = dev.workspace(dims, lay, len(blocks))
+        loops, finals = [], {}
+        for resid, mode in (("bf16", "off"), ("bf16", "conservative"), ("bf16", "extrapolate"),
+                            ("fp32", "off"), ("fp32", "conservative"), ("fp32", "extrapolate")):
+            pol = N.make_policy(mode)
+            stats = {}
+
+            def run():
+                x.copy_(x0)
+                stats["s"] = N.denoise_loop(dims, lay, bw, wl.n_intervals, case.sigmas_video,
+                                            case.sigmas_audio, temb, pol, x, N.DIT_ATTN_VALID_ONLY,
+                                            ws, stream=stream, want_hits=False,
+                                            residual_f32=(resid == "fp32"))[0]
+            ms = gpu_ms(run, warm=1, reps=3)
+            st = stats["s"]
+            finals[(resid, mode)] = x[: wl.n_valid].cpu().numpy()
+            loops.append({"residual": resid, "cache": mode, "ms_per_loop": round(ms, 3),
+                          "steps_per_sec": round(wl.n_intervals / ms * 1e3, 2),
+                          "useful_tflops": round(st.useful_flops / ms / 1e9, 2),
+                          "dit_calls": st.dit_calls, "cache_hits": st.cache_hits})
+        ref = finals[("bf16", "off")]
+        for rec in loops:
+            rec["vs_bf16_off"] = latent_compare(finals[(rec["residual"], rec["cache"])], ref)
+        emit({"workload": "variants", "kind": "variants", "blocks": blocks_rec,
+              "loop": {"workload": wl.name, "intervals": wl.n_intervals, "blocks": wl.n_blocks,
+                       "valid": wl.n_valid, "runs": loops}})
+
     for name, rows_n in (("block_small", None), ("loop_4blk", None), ("block_h3", 256),
                          ("loop_8blk_32k", 256)):
         if want(name):
@@ -492,6 +553,8 @@ def configs_report(args):
         attn_ragged(True)
     if want("rank_share"):
         rank_share()
+    if want("variants"):
+        variants()
 
 
 def hbm_reference(args):
