@@ -60,7 +60,12 @@ TILES = dict(name="block_tiles", hidden=1088, heads=17, head_dim=64, ffn=2880, n
 # slots); the other projections take the 256 x 256 direct-to-LDS tiles.
 KPAD = dict(name="block_kpad", hidden=1088, heads=17, head_dim=64, ffn=2856, n_video=6000,
             n_audio=1500, seq_pad=8192)
-EXTRA = {"block_odd": ODD, "block_tiles": TILES, "block_kpad": KPAD}
+# The widest hidden sizes the boundary accepts, on short sequences: the norm kernels' 8-, 12- and
+# 16-chunk-per-lane instantiations (hidden 4096, 6144, 8192) and the GEMMs at those reductions.
+WIDE = {f"block_wide{d}": dict(name=f"block_wide{d}", hidden=d, heads=d // 128, head_dim=128,
+                               ffn=ffn, n_video=200, n_audio=56, seq_pad=320)
+        for d, ffn in ((4096, 1000), (6144, 1536), (8192, 2048))}
+EXTRA = {"block_odd": ODD, "block_tiles": TILES, "block_kpad": KPAD, **WIDE}
 
 
 def _case(name, seed=0):
@@ -191,6 +196,21 @@ def test_block_kpad_sampled_rows(env):
     rows = np.sort(np.concatenate([rng.choice(V, 44, replace=False), [0, wl.n_video - 1, wl.n_video, V - 1]]))
     check_block(got[rows], x_values(case.x), case.blocks[0], case.temb, wl, "block_kpad sampled rows",
                 rows=rows)
+
+
+@pytest.mark.parametrize("name", sorted(WIDE))
+def test_block_wide_hidden(env, name):
+    """Hidden 4096, 6144 and 8192 (32, 48 and 64 heads of 128) on 256 valid of 320 rows: the whole
+    block output against the oracle."""
+    N, dev = env
+    case = _case(name, seed=4)
+    wl = case.wl
+    V = wl.n_valid
+    say(f"block {name}: D={wl.hidden} H={wl.heads}x{wl.head_dim} F={wl.ffn} L={wl.seq_pad}")
+    out, _, _ = _gpu_block(env, case)
+    got = dev.bf16_values_of(out).astype(np.float64)
+    assert np.all(got[V:] == 0)
+    check_block(got, x_values(case.x), case.blocks[0], case.temb, wl, f"{name} block output")
 
 
 @pytest.mark.parametrize("name", ["block_small", "block_odd"])
