@@ -111,7 +111,9 @@ __global__ __launch_bounds__(256) void k_head_prep(HeadPrepArgs a) {
 template <bool F32IN, int BM>
 __global__ __launch_bounds__(256) void k_head_proj(HeadProjArgs a) {
   constexpr int XRING = F32IN ? 3 : 4;           // x tiles resident or in flight
-  constexpr int WS = 3;                          // weight tiles resident or in flight
+  // weight tiles resident or in flight: two for 64-row bf16 tiles, so that two workgroups fit in
+  // a CU's LDS (measured 74-77 -> 71 us on the 32k-token head against one 128-row workgroup per CU)
+  constexpr int WS = (!F32IN && BM == 64) ? 2 : 3;
   constexpr int ESZ = F32IN ? 4 : 2;
   constexpr int W_STAGE = kHeadBN * kHeadRowB;   // 16 KB
   constexpr int XRAW = BM * kHeadBK * ESZ;       // one x tile as loaded
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256) void k_head_proj(HeadProjArgs a) {
   static_assert(XRING >= WS, "an x tile is never issued after its weight tile");
   __shared__ u32x4 smem[(XRING * XRAW + (F32IN ? 2 * XBF : 0) + WS * W_STAGE) / 16];
   __shared__ float rsq[BM];
-  __shared__ f32x4 mul_s[kHeadMaxD / 4];  // mul of this modality
+  extern __shared__ f32x4 mul_s[];  // mul of this modality: D floats of dynamic LDS
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
@@ -373,39 +375,23 @@ hipError_t launch_head_prep(const HeadPrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (queried once; 256 on MI355X).
-static int head_compute_units() {
-  static const int n = [] {
-    int dev = 0, cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cu <= 0)
-      return 256;
-    return cu;
-  }();
-  return n;
-}
-
 hipError_t launch_head_proj(const HeadProjArgs& a, hipStream_t s) {
-  const int num_cus = head_compute_units();
   if (a.D <= 0 || (a.D % kHeadBK) != 0 || a.D > kHeadMaxD || a.C <= 0 || (a.C & 7) != 0 ||
       (a.ldv & 3) != 0)
     return hipErrorInvalidValue;
   for (int m = 0; m < 2; ++m)
     if (a.rows[m] < 0 || a.valid[m] < 0 || a.valid[m] > a.rows[m]) return hipErrorInvalidValue;
   const int ny = (a.C + kHeadBN - 1) / kHeadBN;
-  // bf16 rows: 128-row tiles when they fill three quarters of the CUs, else 64-row tiles (more
-  // workgroups streaming x); fp32 rows: 64-row tiles (their loaded tiles are twice as large)
-  const int64_t t128 = (int64_t)((a.rows[0] + 127) / 128 + (a.rows[1] + 127) / 128) * ny;
-  const int bm = (!a.x_f32 && t128 * 4 >= (int64_t)num_cus * 3) ? 128 : 64;
+  // 64-row tiles: for bf16 rows two workgroups share a CU (8 waves streaming x)
+  const int bm = 64;
   HeadProjArgs b = a;
   b.tiles0 = (a.rows[0] + bm - 1) / bm;
   const int tiles = b.tiles0 + (a.rows[1] + bm - 1) / bm;
   if (tiles == 0) return hipSuccess;
   const dim3 grid(tiles, ny);
-  if (bm == 128) hipLaunchKernelGGL((k_head_proj<false, 128>), grid, dim3(256), 0, s, b);
-  else if (a.x_f32) hipLaunchKernelGGL((k_head_proj<true, 64>), grid, dim3(256), 0, s, b);
-  else hipLaunchKernelGGL((k_head_proj<false, 64>), grid, dim3(256), 0, s, b);
+  const size_t dyn = (size_t)a.D * sizeof(float);  // the folded scale of the modality
+  if (a.x_f32) hipLaunchKernelGGL((k_head_proj<true, 64>), grid, dim3(256), dyn, s, b);
+  else hipLaunchKernelGGL((k_head_proj<false, 64>), grid, dim3(256), dyn, s, b);
   return hipGetLastError();
 }
 

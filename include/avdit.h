@@ -31,7 +31,7 @@
  *    [rows, F] (rows = all rows of the call, batch * seq_pad for a batch); one request's
  *    q/k/v rows [seq_pad, 3D] (at hidden 3072: seq_pad <= 116,508). The workspace-size
  *    functions apply the same limits and return 0. (The velocity head addresses its input
- *    per 64 or 128 rows, and one modality's weight [C, D] stays below 1 GiB: no limit.)
+ *    per 64 rows, and one modality's weight [C, D] stays below 1 GiB: no limit.)
  *  - Errors: every argument is validated before anything is enqueued. On failure
  *    nothing is enqueued, a negative status is returned and dit_last_error() describes
  *    it. A launch failure reported by the runtime after enqueueing maps to
