@@ -111,6 +111,9 @@ def _oracle(wl, hp, x, temb, bias=True, f32=False, rows=None):
     # 64-wide k-tiles (320)
     (256, 300, 44, 384, 264, True, False),
     (320, 200, 50, 256, 64, True, False),
+    # the widest hidden size the boundary accepts: the folded scale fills the most LDS
+    (8192, 150, 40, 256, 128, True, False),
+    (8192, 100, 60, 192, 128, True, True),
 ])
 def test_head_against_oracle(env, D, nv, na, L, C, bias, f32):
     import oracle as O
